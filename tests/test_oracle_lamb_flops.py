@@ -1,0 +1,108 @@
+"""Pins of the LAMB and FLOP/MFU oracle functions: the hand-derived worked
+example (tests/golden/lamb_worked.json), closed forms at step 1, the
+trust-ratio invariant, and the numbers the MegaScale study guide prints."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import flops, lamb, ptb
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "lamb_worked.json")
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-6, weight_decay=0.01)
+
+
+def _f(a):
+    return np.array([float(x) for x in a])
+
+
+def test_lamb_worked_examples():
+    doc = json.load(open(GOLD))
+    for case in doc["cases"]:
+        w = _f(case["w0"])
+        m = v = np.zeros_like(w)
+        for t, (g, ref) in enumerate(zip(case["grads"], case["steps"]), start=1):
+            w, m, v, r, u = lamb.lamb_tensor_step(w, _f(g), m, v, t, **HP)
+            np.testing.assert_allclose(m, _f(ref["m"]), rtol=1e-15)
+            np.testing.assert_allclose(v, _f(ref["v"]), rtol=1e-15)
+            np.testing.assert_allclose(u, _f(ref["u"]), rtol=1e-13)
+            assert r == pytest.approx(float(ref["ratio"]), rel=1e-13)
+            np.testing.assert_allclose(w, _f(ref["w"]), rtol=1e-14)
+
+
+def test_lamb_step1_closed_form():
+    """At t = 1 from m = v = 0: m_hat = g, v_hat = g^2, so
+    u = g / (|g| + eps) + wd * w."""
+    rng = np.random.default_rng(0)
+    w, g = rng.standard_normal(50), 1e-3 * rng.standard_normal(50)
+    wn, mn, vn, r, u = lamb.lamb_tensor_step(w, g, 0 * w, 0 * w, 1, **HP)
+    u_ref = g / (np.abs(g) + HP["eps"]) + HP["weight_decay"] * w
+    np.testing.assert_allclose(u, u_ref, rtol=1e-12)
+    r_ref = np.linalg.norm(w) / np.linalg.norm(u_ref)
+    assert r == pytest.approx(r_ref, rel=1e-13)
+    np.testing.assert_allclose(wn, w - HP["lr"] * r_ref * u_ref, rtol=1e-14)
+
+
+def test_lamb_sign_descent_special_case():
+    """eps = wd = 0 at t = 1: u = sign(g), ||u|| = sqrt(n), step = lr ||w|| / sqrt(n) per element."""
+    rng = np.random.default_rng(1)
+    w, g = rng.standard_normal(64), rng.standard_normal(64)
+    hp = dict(HP, eps=0.0, weight_decay=0.0)
+    wn, _, _, r, u = lamb.lamb_tensor_step(w, g, 0 * w, 0 * w, 1, **hp)
+    np.testing.assert_allclose(u, np.sign(g), rtol=1e-15)
+    np.testing.assert_allclose(wn, w - hp["lr"] * np.linalg.norm(w) / 8.0 * np.sign(g), rtol=1e-14)
+
+
+def test_lamb_update_norm_invariant():
+    """||w' - w|| = lr * ||w|| whenever both norms are nonzero (any step)."""
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal(100)
+    m, v = 1e-3 * rng.standard_normal(100), 1e-6 * rng.random(100)
+    for t in (1, 3, 10):
+        g = 1e-3 * rng.standard_normal(100)
+        wn, m, v, r, _ = lamb.lamb_tensor_step(w, g, m, v, t, **HP)
+        assert np.linalg.norm(wn - w) == pytest.approx(HP["lr"] * np.linalg.norm(w), rel=1e-12)
+        w = wn
+
+
+def test_lamb_zero_grad_and_zero_weight():
+    # zero gradient and zero weight: u = 0 so both norms vanish, ratio 1, no change
+    out = lamb.lamb_step([dict(w=np.zeros(3), g=np.zeros(3), m=np.zeros(3), v=np.zeros(3))], 1, **HP)
+    assert out[0]["ratio"] == 1.0
+    np.testing.assert_array_equal(out[0]["w"], 0.0)
+    # per-tensor weight decay override
+    w = np.array([1.0, -2.0])
+    o1 = lamb.lamb_step([dict(w=w, g=np.zeros(2), m=np.zeros(2), v=np.zeros(2), weight_decay=0.0)], 1, **HP)
+    np.testing.assert_array_equal(o1[0]["w"], w)   # u = 0 -> ratio 1, no step
+
+
+# ---------------------------------------------------------------- FLOPs / MFU
+def test_mfu_worked_example_from_page():
+    """The study guide's check on Table 2's 12,288-GPU row: 1.984e6 tokens/s
+    x 6 x 1.75e11 = 2.08e18 FLOP/s, and at 312 TFLOP/s per GPU MFU = 54.3%."""
+    assert flops.model_flops(1.75e11, 1.984e6) == pytest.approx(2.08e18, rel=5e-3)
+    assert flops.mfu(1.984e6, 1.75e11, 12288, 312e12) == pytest.approx(0.543, abs=5e-4)
+
+
+def test_table1_parameter_counts():
+    """Table 1: 175B has hidden 12288 and 96 layers, 530B hidden 20480 and 105 layers."""
+    assert flops.dense_params(12288, 96) == pytest.approx(175e9, rel=0.01)
+    assert flops.dense_params(20480, 105) == pytest.approx(530e9, rel=0.01)
+    assert flops.shard_matrix_params(12288, 1536, 6144) == 12 * 12288 ** 2 // 8 == 226_492_416
+    assert flops.shard_matrix_params(20480, 2560, 10240) == 12 * 20480 ** 2 // 8 == 629_145_600
+
+
+@pytest.mark.parametrize("s,w", [(1, 1), (7, 3), (16, 16), (16, 40), (2048, 512)])
+def test_band_pairs_brute_force(s, w):
+    assert flops.band_pairs(s, w) == int(ptb.swa_visible(s, w).sum()) if s <= 64 else True
+    if s > 64:
+        assert flops.band_pairs(s, w) == sum(min(i + 1, w) for i in range(s))
+    assert flops.band_pairs(s, s) == s * (s + 1) // 2
+
+
+def test_attention_flops_175b():
+    # 16 heads of 96 at s = 2048: 917,760 band pairs per head at w = 512
+    assert flops.band_pairs(2048, 512) == 917_760
+    assert flops.attention_flops_fwd(1, 2048, 16, 96, 512) == pytest.approx(4 * 96 * 917_760 * 16)
