@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""One training step of one tensor-parallel shard of the parallel transformer
+block with sliding-window attention, on one MI355X:
+
+    ptb_forward + ptb_backward + lamb_step (over the shard's six parameter
+    tensors, refreshing the bf16 weights the next forward reads)
+
+timed with HIP events on the stream the library launches on.  The forward
+and backward run as their stage entry points (exactly what ptb_forward /
+ptb_backward execute) so that every kernel stage gets its own events.
+
+Prints ONE JSON line.  `value` is the block's model TFLOP/s, 6 * N * T FLOP
+(N = matrix parameters of the shard, T = tokens; the 6N-per-token estimate of
+the MegaScale study guide, ch.2 §2.1) over the measured fwd+bwd time; `mfu`
+divides it by the bf16 dense MFMA peak; `lamb_gbps` is the LAMB step's
+algorithmic bytes over its time.  `roofline` describes the dominant kernel
+stage; `cpu_baseline` times the fp64 CPU oracle on one full step's forward and
+backward of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config 175b_w512]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "PTB+SWA layer fwd+bwd TFLOP/s & MFU at 175B TP=8 shard; LAMB step GB/s"
+PEAK_BF16 = 2.5e15       # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12        # MI355X HBM3E, bytes/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="175b_w512")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the fp64 CPU oracle")
+    p.add_argument("--out", default=None, help="also write the JSON line to this file")
+    return p.parse_args()
+
+
+def stage_flops(cfg):
+    """Algorithmic FLOPs of each stage (GEMMs 2*M*N*K; attention over the band)."""
+    T, h, A, F = cfg.tokens, cfg.hidden, cfg.attn_width, cfg.ffn
+    N1, K2 = 3 * A + F, A + F
+    w = min(cfg.window, cfg.seq)
+    pairs = (w * (w + 1) // 2 + (cfg.seq - w) * w) * cfg.batch * cfg.n_heads
+    att_fwd = 4.0 * cfg.head_dim * pairs          # QK^T and PV
+    return {
+        "fwd.layernorm": 0.0,
+        "fwd.gemm_in": 2.0 * T * N1 * h,
+        "fwd.attention": att_fwd,
+        "fwd.gemm_out": 2.0 * T * K2 * h,
+        "bwd.gemm_dcat": 2.0 * T * K2 * h,
+        "bwd.gemm_dw_out": 2.0 * K2 * h * T,
+        "bwd.attention": 2.0 * att_fwd,           # dV, dP, dQ, dK (recompute not counted)
+        "bwd.gemm_dw_in": 2.0 * N1 * h * T,
+        "bwd.gemm_dxn": 2.0 * T * h * N1,
+        "bwd.layernorm": 0.0,
+    }
+
+
+def lamb_bytes(params):
+    """Algorithmic HBM bytes of one lamb_step: pass A reads w, g, m, v and
+    writes m, v; pass B reads w, m, v, writes w (and the bf16 copy)."""
+    total = 0
+    for p in params:
+        n = p["w"].numel()
+        g = p["g"].element_size()
+        total += n * (4 + g + 4 + 4 + 4 + 4)            # pass A
+        total += n * (12 + 4 + (2 if p.get("w_bf16") is not None else 0))  # pass B
+    return total
+
+
+def cpu_baseline(cfg, inputs, model_flops):
+    """The fp64 oracle's forward + backward of one full step of the workload."""
+    from oracle import ptb as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    d = O.dims_of(cfg)
+    t0 = time.perf_counter()
+    y, saved = O.ptb_forward(d, inputs["x"], inputs["gamma"], inputs["beta"], inputs["w_in"],
+                             inputs["w_out"])
+    O.ptb_backward(d, inputs["x"], inputs["gamma"], inputs["w_in"], inputs["w_out"], saved,
+                   inputs["dy"])
+    dt = time.perf_counter() - t0
+    return {"value": round(model_flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"one full forward+backward of the {cfg.name} shard ({cfg.tokens} tokens) "
+                      f"in fp64 numpy, model FLOPs 6*N*T over its wall time"}
+
+
+def traffic_for(kernel_stage):
+    """HBM bytes per launch of the dominant stage from the committed counter
+    summary, or None when absent or taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "transformer_block_lamb_amd", "csrc", "gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("gemm_source_sha256") != digest:
+        return None
+    return rec.get("stages", {}).get(kernel_stage)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's shard only: the tensor-parallel collectives are not "
+              "part of this library, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from transformer_block_lamb_amd import binding as B
+    from transformer_block_lamb_amd.device import PtbShard
+    from transformer_block_lamb_amd.synth import CONFIGS, LAMB_HPARAMS, ptb_inputs
+
+    cfg = CONFIGS[args.config]
+    inputs = ptb_inputs(cfg)
+    shard = PtbShard(cfg, inputs)
+    A, F = cfg.attn_width, cfg.ffn
+    dev = "cuda"
+    w_in_m = torch.from_numpy(inputs["w_in"]).to(dev)     # fp32 masters
+    w_out_m = torch.from_numpy(inputs["w_out"]).to(dev)
+    hp = LAMB_HPARAMS
+    wd = hp["weight_decay"]
+
+    def tensor(w, g, copy=None):
+        return dict(w=w, g=g, m=torch.zeros_like(w), v=torch.zeros_like(w), w_bf16=copy,
+                    weight_decay=wd)
+
+    params = [tensor(w_in_m[:3 * A], shard.dw_in[:3 * A], shard.w_in[:3 * A]),     # W_qkv
+              tensor(w_in_m[3 * A:], shard.dw_in[3 * A:], shard.w_in[3 * A:]),     # W_fc1
+              tensor(w_out_m[:A], shard.dw_out[:A], shard.w_out[:A]),              # W_o
+              tensor(w_out_m[A:], shard.dw_out[A:], shard.w_out[A:]),              # W_fc2
+              tensor(shard.gamma, shard.dgamma), tensor(shard.beta, shard.dbeta)]
+    desc = B.lamb_tensors(params)
+    lscratch = torch.empty(B.lamb_scratch_bytes(desc), dtype=torch.uint8, device=dev)
+    ratios = torch.empty(len(params), dtype=torch.float32, device=dev)
+
+    names = [f"fwd.{n}" for n in B.FWD_STAGES] + [f"bwd.{n}" for n in B.BWD_STAGES] + ["lamb"]
+
+    def step(it, events=None):
+        k = 0
+        for s in range(len(B.FWD_STAGES)):
+            if events is not None:
+                events[k].record(); k += 1
+            shard.forward_stage(s)
+        for s in range(len(B.BWD_STAGES)):
+            if events is not None:
+                events[k].record(); k += 1
+            shard.backward_stage(s)
+        if events is not None:
+            events[k].record(); k += 1
+        B.lamb_step(desc, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], it, ratios, lscratch)
+        if events is not None:
+            events[k].record()
+
+    for it in range(1, args.warmup + 1):
+        step(it)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + 1 + k, ev[k])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    per_stage = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
+                 for i, n in enumerate(names)}
+    step_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)]))
+    fwd_ms = sum(v for n, v in per_stage.items() if n.startswith("fwd."))
+    bwd_ms = sum(v for n, v in per_stage.items() if n.startswith("bwd."))
+    lamb_ms = per_stage["lamb"]
+
+    flops = stage_flops(cfg)
+    n_mat = (3 * A + F) * cfg.hidden + (A + F) * cfg.hidden
+    model_flops = 6.0 * n_mat * cfg.tokens
+    value = model_flops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+    executed = sum(flops.values()) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+    lb = lamb_bytes(params)
+
+    dom = max((n for n in names if n != "lamb"), key=lambda n: per_stage[n])
+    achieved = flops[dom] / (per_stage[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": round(achieved / (PEAK_BF16 / 1e12), 4),
+                "traffic": traffic_for(dom), "flop_per_launch": flops[dom],
+                "ms_per_launch": round(per_stage[dom], 4)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, random init)",
+        "config": {"workload": f"{cfg.name}: one TP=8 shard, batch {cfg.batch}, seq {cfg.seq}, "
+                               f"hidden {cfg.hidden}, {cfg.n_heads} heads x {cfg.head_dim}, "
+                               f"ffn {cfg.ffn}, window {cfg.window}; LAMB over its 6 tensors",
+                   "global_batch": cfg.batch, "seq_len": cfg.seq, "parallelism": "tp8-shard"},
+        "mfu": round(value / (PEAK_BF16 / 1e12), 4),
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "lamb_ms": round(lamb_ms, 4),
+        "lamb_gbps": round(lb / (lamb_ms * 1e-3) / 1e9, 1),
+        "lamb_hbm_frac": round(lb / (lamb_ms * 1e-3) / PEAK_HBM, 4),
+        "lamb_bytes": lb, "executed_tflops": round(executed, 2),
+        "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4),
+        "stages_ms": {n: round(v, 4) for n, v in per_stage.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inputs, model_flops)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -20,8 +20,9 @@ design notes of the repository):
     w keys including the query itself (fewer at the start of a sequence) and
     w >= s is plain causal attention;
   * softmax scale 1/sqrt(d);
-  * w_in rows are Q | K | V | FC1 (each of Q, K, V head-major); w_out columns
-    are attention (head-major) | FC2;
+  * w_in [3*H*d + F, hidden] rows are Q | K | V | FC1 (each of Q, K, V
+    head-major); w_out [H*d + F, hidden] rows are the attention output
+    projection (head-major) | FC2, so y = [O | GeLU(f)] @ w_out;
   * tensor parallel shard: the shard returns x + its partial sum when
     add_residual is set, else the pure partial sum.
 
@@ -177,7 +178,7 @@ def attn_branch(dims, xn, w_in, w_out):
     k = xn @ w_in[A:2 * A].T
     v = xn @ w_in[2 * A:3 * A].T
     o, _, _ = attention(dims, q, k, v)
-    return o @ w_out[:, :A].T
+    return o @ w_out[:A]
 
 
 def mlp_branch(dims, xn, w_in, w_out):
@@ -185,7 +186,7 @@ def mlp_branch(dims, xn, w_in, w_out):
     _, _, _, _, A, _ = _split(dims)
     w_in, w_out = _f64(w_in), _f64(w_out)
     f = xn @ w_in[3 * A:].T
-    return gelu(f) @ w_out[:, A:].T
+    return gelu(f) @ w_out[A:]
 
 
 def ptb_forward(dims, x, gamma, beta, w_in, w_out):
@@ -203,7 +204,7 @@ def ptb_forward(dims, x, gamma, beta, w_in, w_out):
     o, probs, lse = attention(dims, q, k, v)
     g = gelu(f)
     cat = np.concatenate([o, g], axis=1)
-    y = cat @ w_out.T
+    y = cat @ w_out
     if dims["add_residual"]:
         y = y + x
     saved = dict(xn=xn, xhat=xhat, mean=mean, rstd=rstd, q=q, k=k, v=v, f=f,
@@ -237,8 +238,8 @@ def ptb_backward(dims, x, gamma, w_in, w_out, saved, dy):
     b, s, H, d, A, _ = _split(dims)
     w_in, w_out, dy = _f64(w_in), _f64(w_out), _f64(dy)
     cat = saved["cat"]
-    dw_out = dy.T @ cat
-    dcat = dy @ w_out
+    dw_out = cat.T @ dy
+    dcat = dy @ w_out.T
     d_o, dg = dcat[:, :A], dcat[:, A:]
     df = dg * gelu_grad(saved["f"])
     dq = np.zeros_like(d_o)

@@ -1,0 +1,100 @@
+"""The C ABI library loads, exports every function the headers declare, and
+rejects invalid arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_block_lamb_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in ("ptb.h", "ptb_ops.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = declared_functions()
+    assert {"ptb_forward", "ptb_backward", "lamb_step"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+    assert names == set(B.EXPORTED)
+
+
+def dims(**kw):
+    base = dict(batch=1, seq=128, hidden=256, n_heads=4, head_dim=64, ffn=1024, window=32,
+                add_residual=1, ln_eps=1e-5, dtype=B.PTB_F32)
+    base.update(kw)
+    return B.PtbDims(*[base[f] for f, _ in B.PtbDims._fields_])
+
+
+def test_workspace_sizes():
+    d = dims()
+    T, h, A, F = 128, 256, 256, 1024
+    saved = B.ptb_saved_bytes(d)
+    assert saved >= 4 * (T * h + T * 3 * A + T * F + T * (A + F)) + 4 * (2 * T + 4 * T)
+    assert B.ptb_scratch_bytes(d) > 0
+    # 175B shard, bf16: saved activations about 189 MB (incl. the xn, q, k residuals)
+    d175 = dims(seq=2048, hidden=12288, n_heads=16, head_dim=96, ffn=6144, window=512, dtype=B.PTB_BF16)
+    assert 185e6 < B.ptb_saved_bytes(d175) < 192e6
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(window=0), -1), (dict(batch=0), -1), (dict(head_dim=80), -2), (dict(hidden=260), -2),
+    (dict(dtype=7), -1), (dict(add_residual=2), -1), (dict(ffn=12), -2), (dict(hidden=40960), -2),
+])
+def test_invalid_dims_rejected_before_launch(bad, status):
+    d = dims(**bad)
+    assert B.ptb_saved_bytes(d) == 0
+    fake = 0x10000
+    r = B.lib().ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert r == status
+
+
+def test_null_unaligned_and_small_workspace_rejected():
+    d = dims()
+    L = B.lib()
+    fake = 0x10000
+    assert L.ptb_forward(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, 1 << 40, None) == -1
+    assert L.ptb_forward(ctypes.byref(d), fake + 2, fake, fake, fake, fake, fake, fake, 1 << 40, None) == -1
+    need = B.ptb_saved_bytes(d)
+    assert L.ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, need - 1, None) == -3
+    need = B.ptb_scratch_bytes(d)
+    assert L.ptb_backward(ctypes.byref(d), fake, fake, fake, fake, fake, 1 << 40, fake, fake, fake,
+                          fake, fake, fake, fake, need - 1, None) == -3
+    assert L.ptb_forward(None, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None) == -1
+
+
+def test_lamb_argument_checks():
+    L = B.lib()
+    fake = 0x10000
+    T = lambda n, **kw: B.LambTensor(kw.get("w", fake), fake, fake, fake, kw.get("wc", None), n,
+                                     0.01, kw.get("gdt", 1))
+    arr = (B.LambTensor * 2)(T(100), T(12, gdt=0))
+    need = L.lamb_scratch_bytes(arr, 2)
+    assert need > 0
+    assert L.lamb_step(arr, 2, 1e-3, 0.9, 0.999, 1e-6, 0, None, fake, need, None) == -1   # step 0
+    assert L.lamb_step(arr, 2, 1e-3, 1.0, 0.999, 1e-6, 1, None, fake, need, None) == -1   # beta1 1
+    assert L.lamb_step(arr, 2, 1e-3, 0.9, 0.999, 1e-6, 1, None, fake, need - 1, None) == -3
+    for bad in (T(100, gdt=5), T(100, w=fake + 4), T(0), T(100, wc=fake + 2)):
+        one = (B.LambTensor * 1)(bad)
+        assert L.lamb_step(one, 1, 1e-3, 0.9, 0.999, 1e-6, 1, None, fake, need, None) == -1
+
+
+def test_component_argument_checks():
+    L = B.lib()
+    fake = 0x10000
+    # bf16 with a contiguous dimension not a multiple of 8
+    assert L.ptb_gemm(1, 0, 0, 16, 16, 12, fake, 12, fake, 16, fake, 16, 0, None) == -2
+    assert L.ptb_gemm(1, 0, 0, 16, 16, 16, fake, 8, fake, 16, fake, 16, 0, None) == -1  # lda < K
+    assert L.ptb_layernorm_forward(1, 4, 12, fake, fake, fake, 1e-5, fake, fake, fake, None) == -1
+    assert B.ptb_status_string(-3).startswith("workspace")

@@ -1,0 +1,137 @@
+"""Parity of each kernel of the block against the fp64 oracle (or, for the
+plain GEMM engine, against the definition sum_k A(m,k) B(n,k) in fp64),
+through the C ABI, on ragged shapes that span several tiles."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ptb as O
+from parity import check
+from transformer_block_lamb_amd import binding as B
+from transformer_block_lamb_amd.device import to_device
+from transformer_block_lamb_amd.synth import bf16_round
+
+pytestmark = pytest.mark.gpu
+
+
+def _dt(name):
+    return (B.PTB_BF16, torch.bfloat16) if name == "bf16" else (B.PTB_F32, torch.float32)
+
+
+def _host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _rand(rng, shape, dtype, scale=1.0):
+    a = (scale * rng.standard_normal(shape)).astype(np.float32)
+    return bf16_round(a) if dtype == "bf16" else a
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,width", [(1, 8), (37, 264), (130, 4104), (64, 12288), (3, 32768)])
+def test_layernorm_forward(dtype, rows, width):
+    print(f"layernorm {dtype} rows={rows} width={width}", flush=True)
+    rng = np.random.default_rng(rows * 7 + width)
+    code, tdt = _dt(dtype)
+    x = _rand(rng, (rows, width), dtype, 2.0)
+    x = bf16_round(x + 0.5) if dtype == "bf16" else x + 0.5
+    g = (1 + 0.1 * rng.standard_normal(width)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(width)).astype(np.float32)
+    xd, gd, bd = to_device(x, tdt), to_device(g, torch.float32), to_device(b, torch.float32)
+    xn = torch.empty_like(xd)
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty_like(mean)
+    B.ptb_layernorm_forward(code, rows, width, xd, gd, bd, 1e-5, xn, mean, rstd)
+    torch.cuda.synchronize()
+    ref, _, rmean, rrstd = O.layernorm(x, g, b, 1e-5)
+    check("xn", _host(xn), ref, dtype)
+    np.testing.assert_allclose(_host(mean), rmean, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(_host(rstd), rrstd, rtol=1e-4)
+
+
+GEMM_SHAPES = [(256, 256, 64), (300, 264, 200), (296, 264, 200), (520, 776, 1032), (40, 24, 8),
+               (1, 8, 8), (8, 16, 3), (264, 520, 777)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("a_layout,b_layout", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_layouts(dtype, a_layout, b_layout, M, N, K):
+    print(f"gemm {dtype} layouts={a_layout}{b_layout} M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    code, tdt = _dt(dtype)
+    a = _rand(rng, (M, K), dtype)
+    b = _rand(rng, (N, K), dtype)
+    ref = a.astype(np.float64) @ b.astype(np.float64).T
+    a_store = a if a_layout == 0 else np.ascontiguousarray(a.T)
+    b_store = b if b_layout == 0 else np.ascontiguousarray(b.T)
+    ad, bd = to_device(a_store, tdt), to_device(b_store, tdt)
+    lda = K if a_layout == 0 else M
+    ldb = K if b_layout == 0 else N
+    if dtype == "bf16" and ((K if a_layout == 0 else M) % 8 or (K if b_layout == 0 else N) % 8 or N % 8):
+        # bf16 operands and outputs move in 16-byte vectors along their rows
+        c = torch.empty((M, N), dtype=tdt, device="cuda")
+        with pytest.raises(B.PtbError) as e:
+            B.ptb_gemm(code, a_layout, b_layout, M, N, K, ad, lda, bd, ldb, c, N, 0)
+        assert e.value.status == -2
+        return
+    for c_f32 in ((0, 1) if dtype == "bf16" else (1,)):
+        c = torch.empty((M, N), dtype=torch.float32 if c_f32 else tdt, device="cuda")
+        B.ptb_gemm(code, a_layout, b_layout, M, N, K, ad, lda, bd, ldb, c, N, c_f32)
+        torch.cuda.synchronize()
+        check(f"C(c_f32={c_f32})", _host(c), ref, dtype)
+
+
+def _swa_case(dtype, batch, seq, H, d, w):
+    rng = np.random.default_rng(batch * 1000 + seq + w + d)
+    A = H * d
+    T = batch * seq
+    qkv = _rand(rng, (T, 3 * A), dtype, 1.5)
+    d_o = _rand(rng, (T, A), dtype)
+    dims = dict(batch=batch, seq=seq, n_heads=H, head_dim=d, window=w)
+    o_ref = np.zeros((T, A))
+    lse_ref = np.zeros((batch, H, seq))
+    dq = np.zeros((T, A)); dk = np.zeros((T, A)); dv = np.zeros((T, A))
+    for bi in range(batch):
+        rows = slice(bi * seq, (bi + 1) * seq)
+        for h in range(H):
+            c = slice(h * d, (h + 1) * d)
+            q, k, v = qkv[rows, c], qkv[rows, A:][:, c], qkv[rows, 2 * A:][:, c]
+            o, p, l = O.swa_head(q, k, v, w)
+            o_ref[rows, c] = o
+            lse_ref[bi, h] = l
+            dq[rows, c], dk[rows, c], dv[rows, c] = O.swa_head_backward(q, k, v, p, d_o[rows, c])
+    return qkv, d_o, o_ref, lse_ref, np.concatenate([dq, dk, dv], axis=1), dims
+
+
+SWA_CASES = [
+    # batch, seq, heads, head_dim, window
+    (1, 128, 2, 64, 32), (2, 200, 3, 96, 50), (1, 333, 2, 128, 333), (1, 260, 2, 96, 1),
+    (2, 130, 1, 64, 1000), (1, 520, 2, 128, 129), (1, 64, 1, 96, 64), (1, 1, 1, 64, 5),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", SWA_CASES)
+def test_swa_forward_backward(dtype, case):
+    batch, seq, H, d, w = case
+    print(f"swa {dtype} batch={batch} seq={seq} H={H} d={d} w={w}", flush=True)
+    code, tdt = _dt(dtype)
+    qkv, d_o, o_ref, lse_ref, dqkv_ref, _ = _swa_case(dtype, batch, seq, H, d, w)
+    dims = B.make_dims(batch, seq, 256, H, d, 256, w, 1, 1e-5, code)
+    A = H * d
+    T = batch * seq
+    qkv_d, do_d = to_device(qkv, tdt), to_device(d_o, tdt)
+    o = torch.empty((T, A), dtype=tdt, device="cuda")
+    lse = torch.empty((batch, H, seq), dtype=torch.float32, device="cuda")
+    B.ptb_swa_forward(dims, qkv_d, o, A, lse)
+    dqkv = torch.empty((T, 3 * A), dtype=tdt, device="cuda")
+    dvec = torch.empty((batch, H, seq), dtype=torch.float32, device="cuda")
+    B.ptb_swa_backward(dims, qkv_d, o, A, do_d, lse, dqkv, dvec)
+    torch.cuda.synchronize()
+    check("O", _host(o), o_ref, dtype)
+    np.testing.assert_allclose(_host(lse), lse_ref, rtol=2e-2 if dtype == "bf16" else 1e-5,
+                               atol=2e-2 if dtype == "bf16" else 1e-5)
+    got = _host(dqkv)
+    for name, sl in (("dq", slice(0, A)), ("dk", slice(A, 2 * A)), ("dv", slice(2 * A, 3 * A))):
+        check(name, got[:, sl], dqkv_ref[:, sl], dtype)

@@ -25,7 +25,7 @@ def micro_inputs(dims, seed=0, wstd=0.3):
                 gamma=1.0 + 0.2 * rng.standard_normal(h),
                 beta=0.2 * rng.standard_normal(h),
                 w_in=wstd * rng.standard_normal((3 * A + F_, h)),
-                w_out=wstd * rng.standard_normal((h, A + F_)),
+                w_out=wstd * rng.standard_normal((A + F_, h)),
                 dy=rng.standard_normal((T, h)))
 
 
@@ -169,20 +169,20 @@ def test_ptb_single_branch_special_cases():
     w_in = torch.tensor(inp["w_in"])
     # MLP only
     w_out = inp["w_out"].copy()
-    w_out[:, :A] = 0
+    w_out[:A] = 0
     y, _ = ptb.ptb_forward(d, inp["x"], inp["gamma"], inp["beta"], inp["w_in"], w_out)
-    mlp = F.linear(F.gelu(F.linear(xn, w_in[3 * A:])), torch.tensor(w_out[:, A:])).numpy()
+    mlp = F.linear(F.gelu(F.linear(xn, w_in[3 * A:])), torch.tensor(w_out[A:].T)).numpy()
     np.testing.assert_allclose(y, inp["x"] + mlp, rtol=1e-11, atol=1e-12)
     # attention only
     w_out = inp["w_out"].copy()
-    w_out[:, A:] = 0
+    w_out[A:] = 0
     y, _ = ptb.ptb_forward(d, inp["x"], inp["gamma"], inp["beta"], inp["w_in"], w_out)
     b, s, H, hd = d["batch"], d["seq"], d["n_heads"], d["head_dim"]
     heads = lambda t: t.reshape(b, s, H, hd).permute(0, 2, 1, 3)
     o = F.scaled_dot_product_attention(heads(F.linear(xn, w_in[:A])), heads(F.linear(xn, w_in[A:2 * A])),
                                        heads(F.linear(xn, w_in[2 * A:3 * A])),
                                        attn_mask=torch_layer.band_mask(s, d["window"]))
-    att = F.linear(o.permute(0, 2, 1, 3).reshape(b * s, A), torch.tensor(w_out[:, :A])).numpy()
+    att = F.linear(o.permute(0, 2, 1, 3).reshape(b * s, A), torch.tensor(w_out[:A].T)).numpy()
     np.testing.assert_allclose(y, inp["x"] + att, rtol=1e-11, atol=1e-12)
 
 
@@ -254,7 +254,8 @@ def test_ptb_backward_matches_autograd_tiny_shape():
 
 # ---------------------------------------------------------------- TP shard semantics
 def test_tensor_parallel_shards_sum_to_full_layer():
-    """A full layer with 8 heads and FFN 64 split into 4 column/row shards:
+    """A full layer with 8 heads and FFN 64 split into 4 shards (row blocks of
+    both weights):
     the shard outputs (residual only on shard 0) sum to the full layer, and so
     do dx, dgamma, dbeta; each shard's weight gradient is a slice of the full one."""
     n_shards, H_full, d, F_full, h = 4, 8, 4, 64, 24
@@ -271,16 +272,16 @@ def test_tensor_parallel_shards_sum_to_full_layer():
         attn_rows = lambda base: np.arange(base + r * As, base + (r + 1) * As)
         rows = np.concatenate([attn_rows(0), attn_rows(A), attn_rows(2 * A),
                                3 * A + np.arange(r * Fs, (r + 1) * Fs)])
-        cols = np.concatenate([np.arange(r * As, (r + 1) * As), A + np.arange(r * Fs, (r + 1) * Fs)])
+        out_rows = np.concatenate([np.arange(r * As, (r + 1) * As), A + np.arange(r * Fs, (r + 1) * Fs)])
         sd = dict(full, n_heads=Hs, ffn=Fs, add_residual=int(r == 0))
-        w_in_s, w_out_s = inp["w_in"][rows], inp["w_out"][:, cols]
+        w_in_s, w_out_s = inp["w_in"][rows], inp["w_out"][out_rows]
         ys, ss = ptb.ptb_forward(sd, inp["x"], inp["gamma"], inp["beta"], w_in_s, w_out_s)
         gs = ptb.ptb_backward(sd, inp["x"], inp["gamma"], w_in_s, w_out_s, ss, inp["dy"])
         ysum = ysum + ys
         for k in gsum:
             gsum[k] = gsum[k] + gs[k]
         np.testing.assert_allclose(gs["dw_in"], gf["dw_in"][rows], rtol=1e-11, atol=1e-12)
-        np.testing.assert_allclose(gs["dw_out"], gf["dw_out"][:, cols], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(gs["dw_out"], gf["dw_out"][out_rows], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(ysum, y, rtol=1e-11, atol=1e-11)
     for k in gsum:
         np.testing.assert_allclose(gsum[k], gf[k], rtol=1e-10, atol=1e-11)

@@ -28,8 +28,8 @@ def layer(dims, x, gamma, beta, w_in, w_out):
     o = F.scaled_dot_product_attention(heads(q), heads(k), heads(v),
                                        attn_mask=band_mask(s, dims["window"]))
     o = o.permute(0, 2, 1, 3).reshape(b * s, A)
-    attn = F.linear(o, w_out[:, :A])
-    mlp = F.linear(F.gelu(f), w_out[:, A:])
+    attn = o @ w_out[:A]
+    mlp = F.gelu(f) @ w_out[A:]
     y = attn + mlp
     if dims["add_residual"]:
         y = y + x

@@ -1,0 +1,391 @@
+// C ABI of the library: argument validation, buffer carving and the launch
+// sequence of the block's forward and backward and of the LAMB step.
+// Declarations and argument documentation: include/ptb.h and
+// include/ptb_ops.h.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ptb.h"
+#include "../../include/ptb_ops.h"
+#include "kernels.h"
+
+using namespace ptb;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxMatrixBytes = (int64_t)1 << 31;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t esize(int dtype) { return dtype == PTB_BF16 ? 2 : 4; }
+
+int check_dims(const ptb_dims* d) {
+  if (d == nullptr) return PTB_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->seq < 1 || d->hidden < 1 || d->n_heads < 1 || d->head_dim < 1 ||
+      d->ffn < 1 || d->window < 1)
+    return PTB_ERR_INVALID_ARG;
+  if (d->dtype != PTB_F32 && d->dtype != PTB_BF16) return PTB_ERR_INVALID_ARG;
+  if (!(d->ln_eps >= 0.0f) || !isfinite(d->ln_eps)) return PTB_ERR_INVALID_ARG;
+  if (d->add_residual != 0 && d->add_residual != 1) return PTB_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128) return PTB_ERR_UNSUPPORTED;
+  if (d->hidden % 8 != 0 || d->ffn % 8 != 0 || d->hidden > 32768) return PTB_ERR_UNSUPPORTED;
+  const int64_t T = (int64_t)d->batch * d->seq;
+  const int64_t A = (int64_t)d->n_heads * d->head_dim;
+  const int64_t N1 = 3 * A + d->ffn, K2 = A + d->ffn;
+  const int64_t e = (int64_t)esize(d->dtype);
+  if (T > INT32_MAX / 4 || N1 > INT32_MAX / 4) return PTB_ERR_UNSUPPORTED;
+  // every matrix addressed by a buffer resource must stay below 2 GiB
+  const int64_t widest = N1 > d->hidden ? N1 : d->hidden;
+  if (T * widest * 4 >= kMaxMatrixBytes || N1 * d->hidden * e >= kMaxMatrixBytes ||
+      K2 * d->hidden * e >= kMaxMatrixBytes)
+    return PTB_ERR_UNSUPPORTED;
+  return PTB_OK;
+}
+
+struct Dims {
+  int64_t T, h, A, F, N1, K2, H, D, S, B;
+  size_t e;
+  explicit Dims(const ptb_dims* d)
+      : T((int64_t)d->batch * d->seq), h(d->hidden), A((int64_t)d->n_heads * d->head_dim),
+        F(d->ffn), N1(3 * A + F), K2(A + F), H(d->n_heads), D(d->head_dim), S(d->seq),
+        B(d->batch), e(esize(d->dtype)) {}
+};
+
+// Saved-activation buffer written by forward, read by backward.
+// For bf16 it also keeps the bf16 rounding residuals of xn and of q, k, so
+// the attention scores are formed at fp32-level accuracy (see the input
+// GEMM and the attention kernels).
+struct SavedLayout {
+  size_t xn, xn_lo, qk_lo, qkv, f, cat, mean, rstd, lse, total;
+  explicit SavedLayout(const Dims& d) {
+    const bool split = d.e == 2;
+    size_t o = 0;
+    xn = o;   o += up(d.T * d.h * d.e);
+    xn_lo = o; o += split ? up(d.T * d.h * 2) : 0;
+    qk_lo = o; o += split ? up(d.T * 2 * d.A * 2) : 0;
+    qkv = o;  o += up(d.T * 3 * d.A * d.e);
+    f = o;    o += up(d.T * d.F * d.e);
+    cat = o;  o += up(d.T * d.K2 * d.e);
+    mean = o; o += up(d.T * 4);
+    rstd = o; o += up(d.T * 4);
+    lse = o;  o += up(d.B * d.H * d.S * 4);
+    total = o;
+  }
+};
+
+// Backward temporaries.
+struct ScratchLayout {
+  size_t d_o, dz, dxn, dvec, gpart, bpart, total;
+  explicit ScratchLayout(const Dims& d) {
+    const int64_t nblk = (d.T + ln_bwd_rows_per_block() - 1) / ln_bwd_rows_per_block();
+    size_t o = 0;
+    d_o = o;   o += up(d.T * d.A * d.e);
+    dz = o;    o += up(d.T * d.N1 * d.e);
+    dxn = o;   o += up(d.T * d.h * 4);
+    dvec = o;  o += up(d.B * d.H * d.S * 4);
+    gpart = o; o += up(nblk * d.h * 4);
+    bpart = o; o += up(nblk * d.h * 4);
+    total = o;
+  }
+};
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+template <typename T>
+const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PTB_OK : PTB_ERR_HIP; }
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr || !aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ptb_status_string(int s) {
+  switch (s) {
+    case PTB_OK: return "ok";
+    case PTB_ERR_INVALID_ARG: return "invalid argument (null/unaligned pointer or bad size)";
+    case PTB_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PTB_ERR_WORKSPACE: return "workspace buffer too small";
+    case PTB_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t ptb_saved_bytes(const ptb_dims* d) {
+  if (check_dims(d) != PTB_OK) return 0;
+  return SavedLayout(Dims(d)).total;
+}
+
+size_t ptb_scratch_bytes(const ptb_dims* d) {
+  if (check_dims(d) != PTB_OK) return 0;
+  return ScratchLayout(Dims(d)).total;
+}
+
+int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const float* ln_gamma,
+                      const float* ln_beta, const void* w_in, const void* w_out, void* y,
+                      void* saved, size_t saved_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != PTB_OK) return st;
+  if (stage < -1 || stage >= PTB_FWD_STAGES) return PTB_ERR_INVALID_ARG;
+  if (!all_aligned({x, ln_gamma, ln_beta, w_in, w_out, y, saved})) return PTB_ERR_INVALID_ARG;
+  const Dims d(dims);
+  const SavedLayout L(d);
+  if (saved_bytes < L.total) return PTB_ERR_WORKSPACE;
+  const int dt = dims->dtype;
+  void* xn = at<char>(saved, L.xn);
+  void* xn_lo = dt == PTB_BF16 ? at<char>(saved, L.xn_lo) : nullptr;
+  void* qk_lo = dt == PTB_BF16 ? at<char>(saved, L.qk_lo) : nullptr;
+  void* qkv = at<char>(saved, L.qkv);
+  void* f = at<char>(saved, L.f);
+  void* cat = at<char>(saved, L.cat);
+  float* mean = at<float>(saved, L.mean);
+  float* rstd = at<float>(saved, L.rstd);
+  float* lse = at<float>(saved, L.lse);
+  const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
+                   3 * d.A, qk_lo};
+  for (int s = (stage < 0 ? 0 : stage); s < (stage < 0 ? PTB_FWD_STAGES : stage + 1); ++s) {
+    hipError_t e = hipSuccess;
+    switch (s) {
+      case PTB_FWD_LAYERNORM:
+        e = launch_ln_fwd(dt, x, ln_gamma, ln_beta, dims->ln_eps, (int)d.T, (int)d.h, xn, xn_lo,
+                          mean, rstd, stream);
+        break;
+      case PTB_FWD_GEMM_IN: {  // [q|k|v|f] = xn w_in^T; GeLU(f) into cat
+        // the q and k column tiles take a second pass over xn_lo (bf16 only)
+        GemmDesc g{(int)d.T, (int)d.N1, (int)d.h, kKContig, kKContig, xn, d.h, w_in, d.h};
+        g.a2 = xn_lo;
+        g.n_split = (int)(2 * d.A);
+        e = launch_gemm_in_fwd(dt, g, qkv, qk_lo, f, cat, (int)d.A, (int)d.F, stream);
+        break;
+      }
+      case PTB_FWD_ATTENTION:
+        e = launch_swa_fwd(dt, sw, cat, d.K2, lse, stream);
+        break;
+      case PTB_FWD_GEMM_OUT: {  // y = [x] + cat w_out
+        const GemmDesc g{(int)d.T, (int)d.h, (int)d.K2, kKContig, kMNContig, cat, d.K2, w_out, d.h};
+        e = launch_gemm_out_fwd(dt, g, x, dims->add_residual, y, stream);
+        break;
+      }
+    }
+    if (e != hipSuccess) return PTB_ERR_HIP;
+  }
+  return PTB_OK;
+}
+
+int ptb_forward(const ptb_dims* dims, const void* x, const float* ln_gamma, const float* ln_beta,
+                const void* w_in, const void* w_out, void* y, void* saved, size_t saved_bytes,
+                hipStream_t stream) {
+  return ptb_forward_stage(dims, -1, x, ln_gamma, ln_beta, w_in, w_out, y, saved, saved_bytes,
+                           stream);
+}
+
+int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const float* ln_gamma,
+                       const void* w_in, const void* w_out, const void* saved, size_t saved_bytes,
+                       const void* dy, void* dx, float* d_ln_gamma, float* d_ln_beta, void* dw_in,
+                       void* dw_out, void* scratch, size_t scratch_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != PTB_OK) return st;
+  if (stage < -1 || stage >= PTB_BWD_STAGES) return PTB_ERR_INVALID_ARG;
+  if (!all_aligned({x, ln_gamma, w_in, w_out, saved, dy, dx, d_ln_gamma, d_ln_beta, dw_in,
+                    dw_out, scratch}))
+    return PTB_ERR_INVALID_ARG;
+  const Dims d(dims);
+  const SavedLayout L(d);
+  const ScratchLayout R(d);
+  if (saved_bytes < L.total || scratch_bytes < R.total) return PTB_ERR_WORKSPACE;
+  const int dt = dims->dtype;
+  const void* xn = at<char>(saved, L.xn);
+  const void* qk_lo = dt == PTB_BF16 ? at<char>(saved, L.qk_lo) : nullptr;
+  const void* qkv = at<char>(saved, L.qkv);
+  const void* f = at<char>(saved, L.f);
+  const void* cat = at<char>(saved, L.cat);
+  const float* mean = at<float>(saved, L.mean);
+  const float* rstd = at<float>(saved, L.rstd);
+  const float* lse = at<float>(saved, L.lse);
+  void* d_o = at<char>(scratch, R.d_o);
+  void* dz = at<char>(scratch, R.dz);
+  float* dxn = at<float>(scratch, R.dxn);
+  float* dvec = at<float>(scratch, R.dvec);
+  float* gpart = at<float>(scratch, R.gpart);
+  float* bpart = at<float>(scratch, R.bpart);
+  const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
+                   3 * d.A, qk_lo};
+  for (int s = (stage < 0 ? 0 : stage); s < (stage < 0 ? PTB_BWD_STAGES : stage + 1); ++s) {
+    hipError_t e = hipSuccess;
+    switch (s) {
+      case PTB_BWD_GEMM_DCAT: {  // dcat = dy w_out^T -> dO | dz[:, 3A:] = dg * GeLU'(f)
+        const GemmDesc g{(int)d.T, (int)d.K2, (int)d.h, kKContig, kKContig, dy, d.h, w_out, d.h};
+        e = launch_gemm_dcat(dt, g, f, d_o, dz, (int)d.A, (int)d.F, stream);
+        break;
+      }
+      case PTB_BWD_GEMM_DW_OUT: {  // dw_out = cat^T dy
+        const GemmDesc g{(int)d.K2, (int)d.h, (int)d.T, kMNContig, kMNContig, cat, d.K2, dy, d.h};
+        e = launch_gemm_store(dt, g, dw_out, d.h, false, stream);
+        break;
+      }
+      case PTB_BWD_ATTENTION:  // -> dz[:, :3A]
+        e = launch_swa_bwd(dt, sw, cat, d.K2, d_o, d.A, lse, dvec, dz, d.N1, stream);
+        break;
+      case PTB_BWD_GEMM_DW_IN: {  // dw_in = dz^T xn
+        const GemmDesc g{(int)d.N1, (int)d.h, (int)d.T, kMNContig, kMNContig, dz, d.N1, xn, d.h};
+        e = launch_gemm_store(dt, g, dw_in, d.h, false, stream);
+        break;
+      }
+      case PTB_BWD_GEMM_DXN: {  // dxn = dz w_in (fp32)
+        const GemmDesc g{(int)d.T, (int)d.h, (int)d.N1, kKContig, kMNContig, dz, d.N1, w_in, d.h};
+        e = launch_gemm_store(dt, g, dxn, d.h, true, stream);
+        break;
+      }
+      case PTB_BWD_LAYERNORM: {  // dx (+ dy), then the deterministic dgamma/dbeta reduce
+        e = launch_ln_bwd(dt, x, ln_gamma, mean, rstd, dxn, dims->add_residual ? dy : nullptr, dx,
+                          gpart, bpart, (int)d.T, (int)d.h, stream);
+        if (e == hipSuccess) {
+          const int nblk = (int)((d.T + ln_bwd_rows_per_block() - 1) / ln_bwd_rows_per_block());
+          e = launch_ln_bwd_reduce(gpart, bpart, nblk, (int)d.h, d_ln_gamma, d_ln_beta, stream);
+        }
+        break;
+      }
+    }
+    if (e != hipSuccess) return PTB_ERR_HIP;
+  }
+  return PTB_OK;
+}
+
+int ptb_backward(const ptb_dims* dims, const void* x, const float* ln_gamma, const void* w_in,
+                 const void* w_out, const void* saved, size_t saved_bytes, const void* dy,
+                 void* dx, float* d_ln_gamma, float* d_ln_beta, void* dw_in, void* dw_out,
+                 void* scratch, size_t scratch_bytes, hipStream_t stream) {
+  return ptb_backward_stage(dims, -1, x, ln_gamma, w_in, w_out, saved, saved_bytes, dy, dx,
+                            d_ln_gamma, d_ln_beta, dw_in, dw_out, scratch, scratch_bytes, stream);
+}
+
+size_t lamb_scratch_bytes(const lamb_tensor* t, int32_t n) {
+  if (t == nullptr || n < 1) return 0;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (t[i].n < 0) return 0;
+    blocks += lamb_blocks_for(t[i].n);
+  }
+  return up((size_t)blocks * 2 * sizeof(float)) + up((size_t)n * sizeof(float));
+}
+
+int lamb_step(const lamb_tensor* t, int32_t n, float lr, float beta1, float beta2, float eps,
+              int64_t step, float* ratios_out, void* scratch, size_t scratch_bytes,
+              hipStream_t stream) {
+  if (t == nullptr || n < 1 || step < 1) return PTB_ERR_INVALID_ARG;
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f &&
+        isfinite(lr)))
+    return PTB_ERR_INVALID_ARG;
+  if (scratch == nullptr || !aligned16(scratch)) return PTB_ERR_INVALID_ARG;
+  if (ratios_out != nullptr && (reinterpret_cast<uintptr_t>(ratios_out) & 3u))
+    return PTB_ERR_INVALID_ARG;
+  int64_t total_blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (t[i].n < 1 || !all_aligned({t[i].w, t[i].g, t[i].m, t[i].v})) return PTB_ERR_INVALID_ARG;
+    if (t[i].w_bf16 != nullptr && !aligned16(t[i].w_bf16)) return PTB_ERR_INVALID_ARG;
+    if (t[i].grad_dtype != PTB_F32 && t[i].grad_dtype != PTB_BF16) return PTB_ERR_INVALID_ARG;
+    if (!isfinite(t[i].weight_decay)) return PTB_ERR_INVALID_ARG;
+    total_blocks += lamb_blocks_for(t[i].n);
+  }
+  if (total_blocks > INT32_MAX / 2) return PTB_ERR_UNSUPPORTED;
+  if (scratch_bytes < lamb_scratch_bytes(t, n)) return PTB_ERR_WORKSPACE;
+  float* partials = static_cast<float*>(scratch);
+  float* ratios = at<float>(scratch, up((size_t)total_blocks * 2 * sizeof(float)));
+
+  LambHyper hp;
+  hp.lr = lr; hp.beta1 = beta1; hp.beta2 = beta2; hp.eps = eps;
+  hp.bc1 = (float)(1.0 - pow((double)beta1, (double)step));
+  hp.bc2 = (float)(1.0 - pow((double)beta2, (double)step));
+  if (!(hp.bc1 > 0.f && hp.bc2 > 0.f)) return PTB_ERR_INVALID_ARG;
+
+  int64_t blk_off = 0;
+  for (int first = 0; first < n; first += kLambMaxTensors) {
+    LambBatch b;
+    memset(&b, 0, sizeof(b));
+    b.ntensors = n - first < kLambMaxTensors ? n - first : kLambMaxTensors;
+    int blk = 0;
+    for (int i = 0; i < b.ntensors; ++i) {
+      const lamb_tensor& ti = t[first + i];
+      b.w[i] = ti.w; b.g[i] = ti.g; b.m[i] = ti.m; b.v[i] = ti.v; b.wc[i] = ti.w_bf16;
+      b.n[i] = ti.n; b.wd[i] = ti.weight_decay; b.gdt[i] = ti.grad_dtype;
+      b.blk_start[i] = blk;
+      blk += (int)lamb_blocks_for(ti.n);
+    }
+    b.blk_start[b.ntensors] = blk;
+    hipError_t e = launch_lamb(b, hp, partials + 2 * blk_off, ratios + first,
+                               ratios_out ? ratios_out + first : nullptr, stream);
+    if (e != hipSuccess) return PTB_ERR_HIP;
+    blk_off += blk;
+  }
+  return PTB_OK;
+}
+
+// ------------------------------------------------------------------ components
+int ptb_layernorm_forward(int32_t dtype, int32_t rows, int32_t width, const void* x,
+                          const float* gamma, const float* beta, float eps, void* xn,
+                          float* mean, float* rstd, hipStream_t stream) {
+  if ((dtype != PTB_F32 && dtype != PTB_BF16) || rows < 1 || width < 8 || width % 8 != 0 ||
+      width > 32768 || !(eps >= 0.f))
+    return PTB_ERR_INVALID_ARG;
+  if (!all_aligned({x, gamma, beta, xn, mean, rstd})) return PTB_ERR_INVALID_ARG;
+  return hip_status(
+      launch_ln_fwd(dtype, x, gamma, beta, eps, rows, width, xn, nullptr, mean, rstd, stream));
+}
+
+int ptb_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t M, int32_t N, int32_t K,
+             const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc,
+             int32_t c_f32, hipStream_t stream) {
+  if ((dtype != PTB_F32 && dtype != PTB_BF16) || M < 1 || N < 1 || K < 1) return PTB_ERR_INVALID_ARG;
+  if ((a_layout != 0 && a_layout != 1) || (b_layout != 0 && b_layout != 1)) return PTB_ERR_INVALID_ARG;
+  if (!all_aligned({a, b, c})) return PTB_ERR_INVALID_ARG;
+  if (ldc < N || lda < (a_layout == 0 ? K : M) || ldb < (b_layout == 0 ? K : N))
+    return PTB_ERR_INVALID_ARG;
+  if (dtype == PTB_BF16) {
+    // 16-byte vectors along the contiguous dimension of each operand
+    if (lda % 8 || ldb % 8 || ldc % 8) return PTB_ERR_UNSUPPORTED;  // + 16-byte output chunks
+    if ((a_layout == 0 ? K : M) % 8 || (b_layout == 0 ? K : N) % 8) return PTB_ERR_UNSUPPORTED;
+    const int64_t ea = a_layout == 0 ? (int64_t)M * lda : (int64_t)K * lda;
+    const int64_t eb = b_layout == 0 ? (int64_t)N * ldb : (int64_t)K * ldb;
+    if (ea * 2 >= kMaxMatrixBytes || eb * 2 >= kMaxMatrixBytes) return PTB_ERR_UNSUPPORTED;
+  } else if (c_f32 == 0) {
+    c_f32 = 1;  // fp32 operands always produce fp32
+  }
+  GemmDesc g{M, N, K, a_layout, b_layout, a, lda, b, ldb};
+  return hip_status(launch_gemm_store(dtype, g, c, ldc, c_f32 != 0, stream));
+}
+
+int ptb_swa_forward(const ptb_dims* dims, const void* qkv, void* o, int64_t ldo, float* lse,
+                    hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != PTB_OK) return st;
+  if (!all_aligned({qkv, o, lse})) return PTB_ERR_INVALID_ARG;
+  const Dims d(dims);
+  if (ldo < d.A || ldo % 8) return PTB_ERR_INVALID_ARG;
+  SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv, 3 * d.A};
+  return hip_status(launch_swa_fwd(dims->dtype, sw, o, ldo, lse, stream));
+}
+
+int ptb_swa_backward(const ptb_dims* dims, const void* qkv, const void* o, int64_t ldo,
+                     const void* d_o, const float* lse, void* dqkv, float* dvec,
+                     hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != PTB_OK) return st;
+  if (!all_aligned({qkv, o, d_o, lse, dqkv, dvec})) return PTB_ERR_INVALID_ARG;
+  const Dims d(dims);
+  if (ldo < d.A || ldo % 8) return PTB_ERR_INVALID_ARG;
+  SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv, 3 * d.A};
+  return hip_status(
+      launch_swa_bwd(dims->dtype, sw, o, ldo, d_o, d.A, lse, dvec, dqkv, 3 * d.A, stream));
+}
+
+}  // extern "C"

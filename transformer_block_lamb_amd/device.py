@@ -1,0 +1,97 @@
+"""Device-buffer helpers over the C ABI: allocate the tensors one layer call
+needs and invoke the library.  Allocation and argument marshalling only."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def torch_dtype(name: str):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def to_device(a: np.ndarray, dtype, device="cuda") -> torch.Tensor:
+    """Copy a host array to the device in `dtype` (bf16-exact values stay exact)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device, dtype=dtype)
+
+
+class PtbShard:
+    """Holds the inputs, parameters, outputs and workspaces of one shard."""
+
+    def __init__(self, cfg, inputs: dict, device="cuda"):
+        self.cfg = cfg
+        self.dims = B.dims_from(cfg)
+        dt = torch_dtype(cfg.dtype)
+        self.dt = dt
+        self.x = to_device(inputs["x"], dt, device)
+        self.gamma = to_device(inputs["gamma"], torch.float32, device)
+        self.beta = to_device(inputs["beta"], torch.float32, device)
+        self.w_in = to_device(inputs["w_in"], dt, device)
+        self.w_out = to_device(inputs["w_out"], dt, device)
+        self.dy = to_device(inputs["dy"], dt, device)
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        self.dgamma = torch.empty_like(self.gamma)
+        self.dbeta = torch.empty_like(self.beta)
+        self.dw_in = torch.empty_like(self.w_in)
+        self.dw_out = torch.empty_like(self.w_out)
+        self.saved = torch.empty(B.ptb_saved_bytes(self.dims), dtype=torch.uint8, device=device)
+        self.scratch = torch.empty(B.ptb_scratch_bytes(self.dims), dtype=torch.uint8, device=device)
+
+    def forward(self, stream=None):
+        B.ptb_forward(self.dims, self.x, self.gamma, self.beta, self.w_in, self.w_out, self.y,
+                      self.saved, stream)
+
+    def backward(self, stream=None):
+        B.ptb_backward(self.dims, self.x, self.gamma, self.w_in, self.w_out, self.saved, self.dy,
+                       self.dx, self.dgamma, self.dbeta, self.dw_in, self.dw_out, self.scratch,
+                       stream)
+
+    def forward_stage(self, stage, stream=None):
+        B.ptb_forward_stage(self.dims, stage, self.x, self.gamma, self.beta, self.w_in,
+                            self.w_out, self.y, self.saved, stream)
+
+    def backward_stage(self, stage, stream=None):
+        B.ptb_backward_stage(self.dims, stage, self.x, self.gamma, self.w_in, self.w_out,
+                             self.saved, self.dy, self.dx, self.dgamma, self.dbeta, self.dw_in,
+                             self.dw_out, self.scratch, stream)
+
+    def outputs(self) -> dict:
+        """Host fp64 copies of every output."""
+        f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+        return dict(y=f(self.y), dx=f(self.dx), dgamma=f(self.dgamma), dbeta=f(self.dbeta),
+                    dw_in=f(self.dw_in), dw_out=f(self.dw_out))
+
+
+class LambState:
+    """Device copies of per-tensor (w, g, m, v) plus the scratch of one step.
+
+    grad_dtype: one name for every tensor, or a list with one name per tensor.
+    bf16_copy: also keep a bf16 copy of each w that the step refreshes."""
+
+    def __init__(self, tensors: list, grad_dtype="bf16", weight_decay=0.01, device="cuda",
+                 bf16_copy=False):
+        gdts = grad_dtype if isinstance(grad_dtype, (list, tuple)) else [grad_dtype] * len(tensors)
+        self.params = []
+        for t, gd in zip(tensors, gdts):
+            p = dict(w=to_device(t["w"], torch.float32, device),
+                     g=to_device(t["g"], torch_dtype(gd), device),
+                     m=to_device(t["m"], torch.float32, device),
+                     v=to_device(t["v"], torch.float32, device),
+                     weight_decay=t.get("weight_decay", weight_decay))
+            if bf16_copy:
+                p["w_bf16"] = torch.empty(p["w"].shape, dtype=torch.bfloat16, device=device)
+            self.params.append(p)
+        self.desc = B.lamb_tensors(self.params)
+        self.scratch = torch.empty(B.lamb_scratch_bytes(self.desc), dtype=torch.uint8,
+                                   device=device)
+        self.ratios = torch.empty(len(tensors), dtype=torch.float32, device=device)
+
+    def step(self, step, lr, beta1, beta2, eps, stream=None):
+        B.lamb_step(self.desc, lr, beta1, beta2, eps, step, self.ratios, self.scratch, stream)
+
+    def set_grads(self, grads: list):
+        for p, g in zip(self.params, grads):
+            p["g"].copy_(torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to(p["g"].dtype))

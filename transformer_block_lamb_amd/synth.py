@@ -19,7 +19,7 @@ The shapes are one tensor-parallel shard (TP=8) of the 175B and 530B layer
 configurations of MegaScale (Table 1 on the MegaScale study-guide page), plus a
 tiny and a small layer.  Weight layouts:
   w_in  [3*H*d + F, hidden]  rows: Q (head-major) | K | V | FC1
-  w_out [hidden, H*d + F]    cols: attention (head-major) | FC2
+  w_out [H*d + F, hidden]    rows: attention output projection (head-major) | FC2
 """
 from __future__ import annotations
 
@@ -77,7 +77,7 @@ CONFIGS = {
 LAMB_175B_TENSORS = (
     ("w_qkv", 3 * 1536 * 12288),
     ("w_fc1", 6144 * 12288),
-    ("w_out", 12288 * 1536),
+    ("w_o", 1536 * 12288),
     ("w_fc2", 12288 * 6144),
     ("ln_gamma", 12288),
     ("ln_beta", 12288),
@@ -88,9 +88,10 @@ LAMB_HPARAMS = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-6, weight_decay=0.01
 def bf16_round(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bf16 (ties to even); return fp32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return (u.astype(np.uint32) << 16).view(np.float32)
+    u = a.view(np.uint32)
+    # finite inputs only: the carry never leaves 32 bits below the NaN range
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -127,7 +128,7 @@ def ptb_inputs(cfg: PtbConfig, seed: int = SEED, ln_affine: str = "unit",
     else:
         raise ValueError(ln_affine)
     w_in = _normal(r[3], (cfg.n_in, h), weight_std)
-    w_out = _normal(r[4], (h, cfg.k_out), weight_std)
+    w_out = _normal(r[4], (cfg.k_out, h), weight_std)
     dy = _normal(r[5], (T, h), 1.0)
     out = dict(x=x, gamma=gamma, beta=beta, w_in=w_in, w_out=w_out, dy=dy)
     if cfg.dtype == "bf16":
