@@ -42,7 +42,21 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the fp64 CPU oracle")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run one plain device-to-device copy of MIB MiB and exit (the "
+                        "reference kernel for scaling HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}))
 
 
 def stage_flops(cfg):
@@ -122,6 +136,9 @@ def main():
         print("bench.py measures one GPU's shard only: the tensor-parallel collectives are not "
               "part of this library, so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch

@@ -261,6 +261,24 @@ struct GemmArgs {
   int16_t perm[kMaxPerm];  // N-tile order (when use_perm)
 };
 
+// Scheduling groups of one pipeline phase: 8 x (1 MFMA, 1 op of kind M1),
+// then 8 x (1 MFMA, 1 op of kind M2) (masks: 0x008 MFMA, 0x020 memory read,
+// 0x100 LDS read, 0x200 LDS write), then a full scheduling barrier.
+template <int M1, int M2>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(M1, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(M2, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // 16 MFMAs of one K=16 step: the wave's 128x128 accumulators.
 __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
                                          const bf16x8_t (&fb)[4]) {
@@ -337,33 +355,34 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     const int cur = kt & 1, nxt = cur ^ 1;
     const bf16_t* As = lds[cur][0] + a_off;
     const bf16_t* Bs = lds[cur][1] + b_off;
-    // sched_barrier(0) keeps the compiler from moving instructions across
-    // phase borders, so each phase's memory operations issue before its MFMAs.
+    // Each phase: one K=16 MFMA group plus the memory work of the pipeline.
+    // The group barriers interleave them (MFMA, memory op, MFMA, ...) so the
+    // MFMAs, which only use fragments read in the previous phase, never wait
+    // on this phase's LDS or memory traffic; sched_barrier(0) closes a phase.
     read_frags(fa[1], fb[1], As, Bs, 1);
     la.store(lds[nxt][0]);
-    __builtin_amdgcn_sched_barrier(0);
     mma_step(acc, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave<0x100, 0x200>();
     read_frags(fa[0], fb[0], As, Bs, 2);
     load_a(kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
     mma_step(acc, fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave<0x100, 0x020>();
     read_frags(fa[1], fb[1], As, Bs, 3);
     lb.store(lds[nxt][1]);
-    __builtin_amdgcn_sched_barrier(0);
     mma_step(acc, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_step(acc, fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave<0x100, 0x200>();
+    // Every wave has now written tile t+1 and read its last fragments of
+    // tile t, so after this barrier the first fragments of tile t+1 can be
+    // read while the last MFMA group of tile t runs from registers.
     __syncthreads();
     read_frags(fa[0], fb[0], lds[nxt][0] + a_off, lds[nxt][1] + b_off, 0);
+    load_b(kt + 2);
+    mma_step(acc, fa[1], fb[1]);
+    interleave<0x100, 0x020>();
   }
   __syncthreads();
 
-// Epilogue, one row of four 32x32 accumulator blocks at a time: each wave
+  // Epilogue, one row of four 32x32 accumulator blocks at a time: each wave
   // stages its 32x128 strip in its own LDS area (fp32; block j at word
   // j*kStageBlk + {0,4,32,36}[j] so the row-chunk reads of the four blocks
   // fall on different banks) with a short fully unrolled loop, then re-reads

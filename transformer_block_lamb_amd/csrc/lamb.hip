@@ -16,7 +16,8 @@
 //            forward                                      (+2 bytes/param)
 // All tensors of a call share one launch per pass (a kernel-argument table
 // of up to 16 tensors; a workgroup finds its tensor from the block ranges).
-// Each thread moves 16-byte vectors (4 fp32) and keeps 4 of them in flight.
+// Each thread moves 16-byte vectors (4 fp32) and keeps 8 of them in flight
+// per array.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,7 +25,7 @@ namespace ptb {
 namespace {
 
 constexpr int kLambThreads = 256;
-constexpr int kLambUnroll = 4;
+constexpr int kLambUnroll = 8;
 constexpr int kLambChunk = kLambThreads * 4 * kLambUnroll;  // elements per workgroup
 
 __device__ __forceinline__ int find_tensor(const LambBatch& b, int blk) {
@@ -137,15 +138,21 @@ __global__ __launch_bounds__(kLambThreads) void lamb_pass_a(LambBatch b, LambHyp
   }
 }
 
-__global__ __launch_bounds__(256) void lamb_finalize(LambBatch b, const float* __restrict__ partials,
-                                                     float* __restrict__ ratios,
-                                                     float* __restrict__ ratios_out) {
-  __shared__ double red[2][4];
+// One workgroup of 1024 threads per tensor; thread i adds partials i,
+// i + 1024, ... in fp64, then the 16 wave sums are added in wave order.
+constexpr int kFinThreads = 1024;
+__global__ __launch_bounds__(kFinThreads) void lamb_finalize(LambBatch b,
+                                                             const float* __restrict__ partials,
+                                                             float* __restrict__ ratios,
+                                                             float* __restrict__ ratios_out) {
+  __shared__ double red[2][kFinThreads / 64];
   const int t = blockIdx.x;
   double sw = 0.0, su = 0.0;
-  for (int blk = b.blk_start[t] + threadIdx.x; blk < b.blk_start[t + 1]; blk += 256) {
-    sw += (double)partials[2 * blk];
-    su += (double)partials[2 * blk + 1];
+#pragma unroll 4
+  for (int blk = b.blk_start[t] + threadIdx.x; blk < b.blk_start[t + 1]; blk += kFinThreads) {
+    const float2 p = *reinterpret_cast<const float2*>(partials + 2 * blk);
+    sw += (double)p.x;
+    su += (double)p.y;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -156,8 +163,8 @@ __global__ __launch_bounds__(256) void lamb_finalize(LambBatch b, const float* _
   if ((threadIdx.x & 63) == 0) { red[0][wid] = sw; red[1][wid] = su; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const double W = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    const double U = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    double W = 0.0, U = 0.0;
+    for (int i = 0; i < kFinThreads / 64; ++i) { W += red[0][i]; U += red[1][i]; }
     const float r = (W > 0.0 && U > 0.0) ? (float)(sqrt(W) / sqrt(U)) : 1.0f;
     ratios[t] = r;
     if (ratios_out != nullptr) ratios_out[t] = r;
@@ -216,8 +223,8 @@ hipError_t launch_lamb(const LambBatch& b, const LambHyper& hp, float* partials,
   hipLaunchKernelGGL(lamb_pass_a, dim3(nblk), dim3(kLambThreads), 0, s, b, hp, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lamb_finalize, dim3(b.ntensors), dim3(256), 0, s, b, (const float*)partials,
-                     ratios, ratios_out);
+  hipLaunchKernelGGL(lamb_finalize, dim3(b.ntensors), dim3(kFinThreads), 0, s, b,
+                     (const float*)partials, ratios, ratios_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lamb_pass_b, dim3(nblk), dim3(kLambThreads), 0, s, b, hp,

@@ -166,21 +166,36 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(
   }
 }
 
-// Column sums of the per-block partials, in block order (deterministic).
-__global__ __launch_bounds__(256) void ln_bwd_reduce_kernel(const float* __restrict__ gpart,
-                                                            const float* __restrict__ bpart,
-                                                            int nblk, int width,
-                                                            float* __restrict__ dgamma,
-                                                            float* __restrict__ dbeta) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= width) return;
+// Column sums of the per-block partials.  A workgroup owns 64 columns; its
+// 16 row groups each add every 16th partial row in order, and the 16 group
+// sums are then added in group order, so the result is deterministic.
+constexpr int kRedCols = 64, kRedGroups = 16;
+__global__ __launch_bounds__(kRedCols * kRedGroups) void ln_bwd_reduce_kernel(
+    const float* __restrict__ gpart, const float* __restrict__ bpart, int nblk, int width,
+    float* __restrict__ dgamma, float* __restrict__ dbeta) {
+  __shared__ float sg_s[kRedGroups][kRedCols], sb_s[kRedGroups][kRedCols];
+  const int cl = threadIdx.x % kRedCols, grp = threadIdx.x / kRedCols;
+  const int c = blockIdx.x * kRedCols + cl;
   float sg = 0.f, sb = 0.f;
-  for (int b = 0; b < nblk; ++b) {
-    sg += gpart[(int64_t)b * width + c];
-    sb += bpart[(int64_t)b * width + c];
+  if (c < width) {
+    for (int b = grp; b < nblk; b += kRedGroups) {
+      sg += gpart[(int64_t)b * width + c];
+      sb += bpart[(int64_t)b * width + c];
+    }
   }
-  dgamma[c] = sg;
-  dbeta[c] = sb;
+  sg_s[grp][cl] = sg;
+  sb_s[grp][cl] = sb;
+  __syncthreads();
+  if (grp == 0 && c < width) {
+    float tg = 0.f, tb = 0.f;
+#pragma unroll
+    for (int g = 0; g < kRedGroups; ++g) {
+      tg += sg_s[g][cl];
+      tb += sb_s[g][cl];
+    }
+    dgamma[c] = tg;
+    dbeta[c] = tb;
+  }
 }
 
 template <typename T, int NV>
@@ -256,8 +271,8 @@ hipError_t launch_ln_bwd(int dtype, const void* x, const float* gamma, const flo
 
 hipError_t launch_ln_bwd_reduce(const float* gpart, const float* bpart, int nblk, int width,
                                 float* dgamma, float* dbeta, hipStream_t s) {
-  hipLaunchKernelGGL(ln_bwd_reduce_kernel, dim3((width + 255) / 256), dim3(256), 0, s, gpart,
-                     bpart, nblk, width, dgamma, dbeta);
+  hipLaunchKernelGGL(ln_bwd_reduce_kernel, dim3((width + kRedCols - 1) / kRedCols),
+                     dim3(kRedCols * kRedGroups), 0, s, gpart, bpart, nblk, width, dgamma, dbeta);
   return hipGetLastError();
 }
 

@@ -227,6 +227,8 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
 }
 
 // ------------------------------------------------------------------ D = rowsum(dO * O)
+// One thread per (batch, head, query); the head's D values of dO and O move
+// as 8-element vectors (D is a multiple of 8).
 template <typename T>
 __global__ __launch_bounds__(256) void swa_rowdot(const T* __restrict__ d_o, int64_t ld_do,
                                                   const T* __restrict__ o, int64_t ldo,
@@ -241,7 +243,13 @@ __global__ __launch_bounds__(256) void swa_rowdot(const T* __restrict__ d_o, int
   const T* a = d_o + t * ld_do + h * D;
   const T* c = o + t * ldo + h * D;
   float s = 0.f;
-  for (int k = 0; k < D; ++k) s += Elt<T>::ld(a + k) * Elt<T>::ld(c + k);
+  for (int k = 0; k < D; k += 8) {
+    float va[8], vc[8];
+    Vec8<T>::load(a + k, va);
+    Vec8<T>::load(c + k, vc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += va[e] * vc[e];
+  }
   dvec[idx] = s;
 }
 
