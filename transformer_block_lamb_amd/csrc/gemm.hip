@@ -261,11 +261,23 @@ struct GemmArgs {
   int16_t perm[kMaxPerm];  // N-tile order (when use_perm)
 };
 
-// Scheduling groups of one pipeline phase: 8 x (1 MFMA, 1 op of kind M1),
-// then 8 x (1 MFMA, 1 op of kind M2) (masks: 0x008 MFMA, 0x020 memory read,
-// 0x100 LDS read, 0x200 LDS write), then a full scheduling barrier.
-template <int M1, int M2>
+// Scheduling groups of one pipeline phase (masks: 0x008 MFMA, 0x020 memory
+// read, 0x100 LDS read, 0x200 LDS write), each closed by a full scheduling
+// barrier: interleave<M>: 8 x (1 MFMA, 1 op M) then the other 8 MFMAs;
+// interleave3<M1, M2, M3>: 8 x (1 MFMA, 1 op M1), then 8 x (1 MFMA, 1 op M2,
+// 1 op M3).
+template <int M>
 __device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(M, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int M1, int M2, int M3>
+__device__ __forceinline__ void interleave3() {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -275,6 +287,7 @@ __device__ __forceinline__ void interleave() {
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(M2, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(M3, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -359,26 +372,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     // The group barriers interleave them (MFMA, memory op, MFMA, ...) so the
     // MFMAs, which only use fragments read in the previous phase, never wait
     // on this phase's LDS or memory traffic; sched_barrier(0) closes a phase.
+    // Each operand's registers are refilled in the same phase that writes
+    // them to LDS, which gives every memory load four phases of lead.
     read_frags(fa[1], fb[1], As, Bs, 1);
     la.store(lds[nxt][0]);
-    mma_step(acc, fa[0], fb[0]);
-    interleave<0x100, 0x200>();
-    read_frags(fa[0], fb[0], As, Bs, 2);
     load_a(kt + 2);
+    mma_step(acc, fa[0], fb[0]);
+    interleave3<0x100, 0x200, 0x020>();
+    read_frags(fa[0], fb[0], As, Bs, 2);
     mma_step(acc, fa[1], fb[1]);
-    interleave<0x100, 0x020>();
+    interleave<0x100>();
     read_frags(fa[1], fb[1], As, Bs, 3);
     lb.store(lds[nxt][1]);
+    load_b(kt + 2);
     mma_step(acc, fa[0], fb[0]);
-    interleave<0x100, 0x200>();
+    interleave3<0x100, 0x200, 0x020>();
     // Every wave has now written tile t+1 and read its last fragments of
     // tile t, so after this barrier the first fragments of tile t+1 can be
     // read while the last MFMA group of tile t runs from registers.
     __syncthreads();
     read_frags(fa[0], fb[0], lds[nxt][0] + a_off, lds[nxt][1] + b_off, 0);
-    load_b(kt + 2);
     mma_step(acc, fa[1], fb[1]);
-    interleave<0x100, 0x020>();
+    interleave<0x100>();
   }
   __syncthreads();
 
