@@ -11,13 +11,13 @@
 //
 // bf16 path (gfx950 MFMA): 256x256 output tile per workgroup of 4 waves, each
 // wave a 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks with fp32
-// accumulators; K step 64; A and B tiles staged through LDS (row stride 72
-// elements so the 16-byte fragment reads of 16 consecutive rows hit distinct
-// banks), double-buffered, with the next tile's global loads in flight during
-// the current tile's MFMAs.  An M/N-contiguous operand is loaded as 8x8
-// blocks and transposed in registers before the LDS store, so the MFMA
-// fragment reads are always K-contiguous.  Edges are masked by the buffer
-// unit's range check (zero fill), so any M, N, K is accepted.
+// accumulators (all 256 AGPRs); K step 32.  Operand tiles go from memory
+// straight into LDS (buffer loads with the LDS bit, no register staging)
+// through a 4-stage ring, so three K tiles of loads are in flight while one
+// is multiplied.  M/N-contiguous operands stay in that layout in LDS and are
+// read with the transposing LDS read (ds_read_b64_tr_b16) into the K-major
+// MFMA fragments.  Edges are masked by the buffer unit's range check (zero
+// fill), so any M, N, K is accepted.
 //
 // Tile order: the hardware deals workgroups round-robin to the 8 XCDs; the
 // block index is remapped so that each XCD gets a contiguous range of tiles,
@@ -32,8 +32,10 @@
 namespace ptb {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDS_LD = BK + 8;      // elements per LDS row
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int kStages = 4;                    // K tiles resident in LDS
+constexpr int kOpBytes = BM * BK * 2;         // one operand tile, 16 KB
+constexpr int kStageBytes = 2 * kOpBytes;     // A tile, then B tile
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;
 
@@ -194,52 +196,96 @@ __device__ __forceinline__ void tile_coords(int bid, int ntm, int ntn, const int
   if (perm != nullptr) tn = perm[tn];
 }
 
-// --------------------------------------------------------------- bf16 loaders
-// One 256 x 64 operand tile (256 rows of the M or N dimension, 64 of K).
+// --------------------------------------------------------------- bf16 operand tiles
+// One operand tile is 256 rows (of M or N) x 32 of K, 16 KB, and reaches LDS
+// by direct buffer->LDS loads (buffer_load_dwordx4 ... lds): one wave
+// instruction writes 1 KB of LDS, lane L's 16 bytes at byte 16 L, so the LDS
+// layout is chosen by which global piece each lane fetches.  Out-of-range
+// lanes (rows past M/N, K past the end) are steered outside the buffer and
+// the load then writes zeros.
+//
+//   K-contiguous operand: LDS row r (64 bytes) holds the 32 K values of tile
+//   row r as four 16-byte slots; logical slot c sits at slot c ^ ((r>>2)&3),
+//   so the 16-byte fragment reads of 16 consecutive rows hit all 64 banks.
+//   M/N-contiguous operand: LDS row k (512 bytes) holds tile K row k; its 16
+//   32-byte pairs (16 M/N values each) are permuted, logical pair P at
+//   P ^ (2 (k&3)), so the transposing fragment reads (ds_read_b64_tr_b16,
+//   4 K rows x 32 bytes per 16 lanes) hit distinct banks.
+constexpr int kDmaPerOp = kOpBytes / (kGemmThreads * 16);  // DMA instructions per lane
+constexpr int kDmaPerTile = 2 * kDmaPerOp;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
 template <int LAY>
-struct TileLoader {
-  uint4 r[8];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int row0, int rows, int k0,
-                                       int K, int64_t ld) {
-    const int t = threadIdx.x;
-    if (LAY == kKContig) {
-      const int c = t & 7, rr = t >> 3;
-      const int k = k0 + c * 8;
+struct DmaOperand {
+  uint32_t base[kDmaPerOp];  // byte offset of this lane's piece in K tile 0
+  int kin[kDmaPerOp];        // K index of the piece inside a tile (2^30 if its row is out)
+  uint32_t kstep;            // bytes from one K tile to the next
+  __device__ __forceinline__ void init(int wave, int lane, int r0, int rows, int64_t ld) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = row0 + rr + 32 * i;
-        const uint32_t off = (row < rows && k < K)
-                                 ? (uint32_t)(((int64_t)row * ld + k) * 2)
-                                 : kOutOfRange;
-        r[i] = buf_load16(rs, off);
+    for (int i = 0; i < kDmaPerOp; ++i) {
+      const int chunk = i * 4 + wave;  // 1 KB of LDS
+      int row, kk;
+      if (LAY == kKContig) {
+        row = 16 * chunk + (lane >> 2);
+        kk = 8 * ((lane & 3) ^ (lane >> 4));
+        base[i] = (uint32_t)(((int64_t)(r0 + row) * ld + kk) * 2);
+      } else {
+        kk = 2 * chunk + (lane >> 5);
+        const int q = lane & 31;
+        row = 8 * (2 * ((q >> 1) ^ (2 * (kk & 3))) + (q & 1));
+        base[i] = (uint32_t)(((int64_t)kk * ld + r0 + row) * 2);
       }
-    } else {
-      const int kb = t & 7, mb = t >> 3;
-      const int row = row0 + mb * 8;
+      kin[i] = r0 + row < rows ? kk : (1 << 30);
+    }
+    kstep = LAY == kKContig ? (uint32_t)(BK * 2) : (uint32_t)(BK * ld * 2);
+  }
+  // K tile kt of the operand into LDS at `op`; pieces at K >= klim load zeros.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* op, int wave, int kt,
+                                        int klim) const {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = k0 + kb * 8 + i;
-        const uint32_t off = (k < K && row < rows)
-                                 ? (uint32_t)(((int64_t)k * ld + row) * 2)
-                                 : kOutOfRange;
-        r[i] = buf_load16(rs, off);
-      }
+    for (int i = 0; i < kDmaPerOp; ++i) {
+      const uint32_t off = kt * BK + kin[i] < klim ? base[i] + (uint32_t)kt * kstep : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(op + (i * 4 + wave) * 1024), 16,
+                                               off, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* lds) const {
-    const int t = threadIdx.x;
+};
+
+// MFMA fragments of one K=16 step for a wave's 128 rows (4 blocks of 32):
+// lane l gets rows 32 i + l%32, K values 8 (l/32) .. +8 of the step.
+template <int LAY>
+struct FragReader {
+  int off[4];
+  __device__ __forceinline__ void init(int lane, int wsel) {
     if (LAY == kKContig) {
-      const int c = t & 7, rr = t >> 3;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<uint4*>(lds + (rr + 32 * i) * LDS_LD + c * 8) = r[i];
+      for (int ks = 0; ks < 2; ++ks)
+        off[ks] = (wsel * 128 + (lane & 31)) * 64 +
+                  16 * ((2 * ks + (lane >> 5)) ^ ((lane >> 2) & 3));
     } else {
-      const int kb = t & 7, mb = t >> 3;
-      uint4 tr[8];
-      transpose8x8(r, tr);
+      // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
+      // element i%4 of the 4-value pieces addressed by lanes 4e + i/4
+      // (e = 0..3), so lane j addresses K row j/4 at M/N offset 4 (j%4).
+      const int g = lane >> 4, j = lane & 15;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint4*>(lds + (mb * 8 + j) * LDS_LD + kb * 8) = tr[j];
+      for (int i = 0; i < 4; ++i)
+        off[i] = (8 * (g >> 1) + (j >> 2)) * 512 +
+                 32 * (8 * wsel + 2 * (i ^ (j >> 2)) + (g & 1)) + 8 * (j & 3);
+    }
+  }
+  __device__ __forceinline__ void read(bf16x8_t (&f)[4], const char* op, int ks) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (LAY == kKContig) {
+        f[i] = *reinterpret_cast<const bf16x8_t*>(op + off[ks] + i * 2048);
+      } else {
+        const char* p = op + off[i] + ks * 8192;
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)p);
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(p + 2048));
+        f[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     }
   }
 };
@@ -261,37 +307,6 @@ struct GemmArgs {
   int16_t perm[kMaxPerm];  // N-tile order (when use_perm)
 };
 
-// Scheduling groups of one pipeline phase (masks: 0x008 MFMA, 0x020 memory
-// read, 0x100 LDS read, 0x200 LDS write), each closed by a full scheduling
-// barrier: interleave<M>: 8 x (1 MFMA, 1 op M) then the other 8 MFMAs;
-// interleave3<M1, M2, M3>: 8 x (1 MFMA, 1 op M1), then 8 x (1 MFMA, 1 op M2,
-// 1 op M3).
-template <int M>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(M, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  __builtin_amdgcn_sched_barrier(0);
-}
-template <int M1, int M2, int M3>
-__device__ __forceinline__ void interleave3() {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(M1, 1, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(M2, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(M3, 1, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // 16 MFMAs of one K=16 step: the wave's 128x128 accumulators.
 __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
                                          const bf16x8_t (&fb)[4]) {
@@ -300,28 +315,54 @@ __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const bf16x8_t (
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
 }
-// This lane's A and B fragments of K step ks from one LDS stage.
-__device__ __forceinline__ void read_frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4],
-                                           const bf16_t* As, const bf16_t* Bs, int ks) {
+
+// Scheduling of one phase (masks: 0x008 MFMA, 0x020 memory read, 0x100 LDS
+// read): the 16 MFMAs, with NR LDS reads and NV memory instructions dealt
+// out after the first MFMAs, closed by a full scheduling barrier.
+template <int NR, int NV>
+__device__ __forceinline__ void interleave() {
+  static_assert(NR <= 16 && NV <= 16, "one of each per MFMA at most");
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    fa[i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * LDS_LD + ks * 16);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    fb[j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * LDS_LD + ks * 16);
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Main loop as a three-stage pipeline over K tiles t = 0, 1, ... (tiles
-// nk1.. of a two-pass tile read a2): while the MFMAs consume tile t from one
-// LDS stage, tile t+1 (already in registers) is written to the other stage
-// and tile t+2 is fetched from memory, split over the four K=16 steps so that
-// LDS and memory instructions sit between MFMAs; the fragments of the next
-// K=16 step are read from LDS one step ahead (two register sets).  Tiles at
-// or beyond the end load out of range (zeros, no memory traffic), so the loop
-// body has no branches.  One barrier per K tile.
+// Wait until at most VM memory instructions of this wave are outstanding and
+// its LDS reads are done, then barrier.  (A plain __syncthreads would wait
+// for every outstanding load, draining the pipeline.)
+template <int VM>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(VM < 64, "vmcnt field");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Main loop: a kStages-deep LDS pipeline over K tiles t = 0, 1, ... (tiles
+// nk1.. of a two-pass tile read a2).  While tile t is multiplied, the loads
+// of tiles t+1 .. t+kStages-1 are in flight; tile t+kStages-1 is issued in
+// the first half of tile t into the stage tile t-1 used.  Each tile is two
+// phases of 16 MFMAs: the first reads the second K=16 step's fragments and
+// issues the loads, then each wave waits for its own loads of tile t+1 and
+// the workgroup meets at the single barrier of the tile; the second phase
+// reads tile t+1's first fragments.  Tiles past the end load zeros (no
+// memory traffic), so the body has no branches; the loop is unrolled by the
+// number of stages so every LDS address is static (K is padded with zero
+// tiles to whole rounds).
 template <int ALAY, int BLAY, class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][2][BM * LDS_LD];
+  // one array per stage, so the compiler sees that loads into one stage do
+  // not alias fragment reads from another
+  __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
+  static_assert(kStages == 4, "stage arrays");
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, ntm, ntn, g.use_perm ? g.perm : nullptr, tm, tn);
@@ -329,8 +370,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, g.a_bytes);
   const __amdgpu_buffer_rsrc_t ra2 = make_rsrc(g.a2 != nullptr ? g.a2 : g.a, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, g.b_bytes);
-  TileLoader<ALAY> la;
-  TileLoader<BLAY> lb;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  DmaOperand<ALAY> da;
+  DmaOperand<BLAY> db;
+  da.init(wave, lane, m0, g.M, g.lda);
+  db.init(wave, lane, n0, g.N, g.ldb);
+  FragReader<ALAY> fra;
+  FragReader<BLAY> frb;
+  fra.init(lane, wm);
+  frb.init(lane, wn);
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -341,60 +390,44 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 
   const int nk1 = (g.K + BK - 1) / BK;
   const int nk = (g.a2 != nullptr && n0 < g.n_split) ? 2 * nk1 : nk1;
-  auto load_a = [&](int t) {
-    const int kk = t < nk1 ? t : t - nk1;
-    la.load(t < nk1 ? ra : ra2, m0, g.M, kk * BK, t < nk ? g.K : 0, g.lda);
+  auto issue = [&](char* st, int t) {
+    const bool second = t >= nk1;
+    const int kt = second ? t - nk1 : t;
+    const int klim = t < nk ? g.K : 0;
+    da.issue(second ? ra2 : ra, st, wave, kt, klim);
+    db.issue(rb, st + kOpBytes, wave, kt, klim);
   };
-  auto load_b = [&](int t) {
-    const int kk = t < nk1 ? t : t - nk1;
-    lb.load(rb, n0, g.N, kk * BK, t < nk ? g.K : 0, g.ldb);
-  };
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int frag_off = (lane & 31) * LDS_LD + (lane >> 5) * 8;
-  const int a_off = wm * 128 * LDS_LD + frag_off, b_off = wn * 128 * LDS_LD + frag_off;
-
-  load_a(0);
-  load_b(0);
-  la.store(lds[0][0]);
-  lb.store(lds[0][1]);
-  load_a(1);
-  load_b(1);
-  __syncthreads();
+  constexpr int kReads = (ALAY == kKContig ? 4 : 8) + (BLAY == kKContig ? 4 : 8);
   bf16x8_t fa[2][4], fb[2][4];
-  read_frags(fa[0], fb[0], lds[0][0] + a_off, lds[0][1] + b_off, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
-    const bf16_t* As = lds[cur][0] + a_off;
-    const bf16_t* Bs = lds[cur][1] + b_off;
-    // Each phase: one K=16 MFMA group plus the memory work of the pipeline.
-    // The group barriers interleave them (MFMA, memory op, MFMA, ...) so the
-    // MFMAs, which only use fragments read in the previous phase, never wait
-    // on this phase's LDS or memory traffic; sched_barrier(0) closes a phase.
-    // Each operand's registers are refilled in the same phase that writes
-    // them to LDS, which gives every memory load four phases of lead.
-    read_frags(fa[1], fb[1], As, Bs, 1);
-    la.store(lds[nxt][0]);
-    load_a(kt + 2);
+  auto tile = [&](const char* cur, const char* nxt, char* dst, int t) {
+    fra.read(fa[1], cur, 1);
+    frb.read(fb[1], cur + kOpBytes, 1);
+    issue(dst, t + kStages - 1);
     mma_step(acc, fa[0], fb[0]);
-    interleave3<0x100, 0x200, 0x020>();
-    read_frags(fa[0], fb[0], As, Bs, 2);
+    interleave<kReads, kDmaPerTile>();
+    wait_barrier<(kStages - 2) * kDmaPerTile>();
+    fra.read(fa[0], nxt, 0);
+    frb.read(fb[0], nxt + kOpBytes, 0);
     mma_step(acc, fa[1], fb[1]);
-    interleave<0x100>();
-    read_frags(fa[1], fb[1], As, Bs, 3);
-    lb.store(lds[nxt][1]);
-    load_b(kt + 2);
-    mma_step(acc, fa[0], fb[0]);
-    interleave3<0x100, 0x200, 0x020>();
-    // Every wave has now written tile t+1 and read its last fragments of
-    // tile t, so after this barrier the first fragments of tile t+1 can be
-    // read while the last MFMA group of tile t runs from registers.
-    __syncthreads();
-    read_frags(fa[0], fb[0], lds[nxt][0] + a_off, lds[nxt][1] + b_off, 0);
-    mma_step(acc, fa[1], fb[1]);
-    interleave<0x100>();
+    interleave<kReads, 0>();
+  };
+
+  issue(st0, 0);
+  issue(st1, 1);
+  issue(st2, 2);
+  wait_barrier<(kStages - 2) * kDmaPerTile>();
+  fra.read(fa[0], st0, 0);
+  frb.read(fb[0], st0 + kOpBytes, 0);
+  // whole rounds of kStages tiles (an exit inside a round makes the
+  // accumulators live across several loop exits, which spills them); the
+  // padding tiles load zeros and add nothing
+  for (int kt = 0; kt < nk; kt += kStages) {
+    tile(st0, st1, st3, kt);
+    tile(st1, st2, st0, kt + 1);
+    tile(st2, st3, st1, kt + 2);
+    tile(st3, st0, st2, kt + 3);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS
   __syncthreads();
 
   // Epilogue, one row of four 32x32 accumulator blocks at a time: each wave
@@ -404,7 +437,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   // it as 8-column row chunks (4 rows x 128 columns per wave instruction) and
   // runs the epilogue in a rolled loop, so every lane issues 16-byte stores.
   constexpr int kStageRow = 36, kStageBlk = 1216;
-  float* stage = reinterpret_cast<float*>(&lds[0][0][0]) + wave * (4 * kStageBlk);
+  static_assert(4 * kStageBlk * 4 <= kStageBytes, "epilogue staging");
+  float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
