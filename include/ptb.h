@@ -79,10 +79,13 @@ typedef struct {
 
 /* Bytes of the `saved` buffer that ptb_forward fills and ptb_backward reads
  * (LN output and statistics, Q|K|V, FC1 pre-activation, [O | GeLU(FC1)],
- * attention log-sum-exp).  0 if dims are invalid. */
+ * attention log-sum-exp; for bf16 also the rounding residuals of the LN
+ * output and of q, k, and a 128 MiB tail that the forward GEMMs use as
+ * workspace for split-K partial tiles).  0 if dims are invalid. */
 size_t ptb_saved_bytes(const ptb_dims* dims);
 
-/* Bytes of the temporary `scratch` buffer ptb_backward needs.  0 if invalid. */
+/* Bytes of the temporary `scratch` buffer ptb_backward needs (bf16: including
+ * 128 MiB of GEMM split-K workspace).  0 if invalid. */
 size_t ptb_scratch_bytes(const ptb_dims* dims);
 
 /* Forward of one shard ([MS] PTB and SWA rows):

@@ -63,11 +63,19 @@ int ptb_layernorm_forward(int32_t dtype, int32_t rows, int32_t width, const void
  *   a_layout 0: A(m, k) = a[m*lda + k]      1: A(m, k) = a[k*lda + m]
  *   b_layout 0: B(n, k) = b[n*ldb + k]      1: B(n, k) = b[k*ldb + n]
  *   C row-major with leading dimension ldc, in `dtype`, or fp32 when c_f32.
- * bf16: the contiguous dimension of each operand and lda, ldb must be
- * multiples of 8, and each operand below 2 GiB.  fp32 operands give fp32 C. */
+ * bf16: the contiguous dimension of each operand and lda, ldb, ldc must be
+ * multiples of 8, and each operand below 2 GiB.  fp32 operands give fp32 C.
+ * workspace (bf16 only, may be NULL; device memory, 256-byte aligned, at
+ * least ptb_gemm_workspace_bytes(), owned by the caller, contents need not
+ * be initialised): with it, shapes whose tile count leaves CUs idle are
+ * split along K across all CUs (stream-K) and the partial tiles are summed
+ * in a fixed order, so results stay deterministic.  Calls that share a
+ * workspace must be ordered on one stream.  A workspace that is too small or
+ * misaligned gives PTB_ERR_WORKSPACE. */
+size_t ptb_gemm_workspace_bytes(void);
 int ptb_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t M, int32_t N, int32_t K,
              const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc,
-             int32_t c_f32, hipStream_t stream);
+             int32_t c_f32, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Sliding-window attention forward (SWA row: key j visible to query i iff
  * 0 <= i - j < window; scale 1/sqrt(head_dim)).  qkv [batch*seq, 3*H*d] in

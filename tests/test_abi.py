@@ -43,9 +43,15 @@ def test_workspace_sizes():
     saved = B.ptb_saved_bytes(d)
     assert saved >= 4 * (T * h + T * 3 * A + T * F + T * (A + F)) + 4 * (2 * T + 4 * T)
     assert B.ptb_scratch_bytes(d) > 0
-    # 175B shard, bf16: saved activations about 189 MB (incl. the xn, q, k residuals)
+    # 175B shard, bf16: saved activations about 189 MB (incl. the xn, q, k
+    # residuals) plus the 128 MiB GEMM workspace tail
     d175 = dims(seq=2048, hidden=12288, n_heads=16, head_dim=96, ffn=6144, window=512, dtype=B.PTB_BF16)
-    assert 185e6 < B.ptb_saved_bytes(d175) < 192e6
+    ws = B.ptb_gemm_workspace_bytes()
+    assert ws == 2 * 256 * 256 * 256 * 4
+    assert 185e6 < B.ptb_saved_bytes(d175) - ws < 192e6
+    assert B.ptb_scratch_bytes(d175) > ws
+    # fp32 has no split-K workspace
+    assert B.ptb_saved_bytes(d) < ws
 
 
 @pytest.mark.parametrize("bad,status", [
@@ -94,7 +100,10 @@ def test_component_argument_checks():
     L = B.lib()
     fake = 0x10000
     # bf16 with a contiguous dimension not a multiple of 8
-    assert L.ptb_gemm(1, 0, 0, 16, 16, 12, fake, 12, fake, 16, fake, 16, 0, None) == -2
-    assert L.ptb_gemm(1, 0, 0, 16, 16, 16, fake, 8, fake, 16, fake, 16, 0, None) == -1  # lda < K
+    assert L.ptb_gemm(1, 0, 0, 16, 16, 12, fake, 12, fake, 16, fake, 16, 0, None, 0, None) == -2
+    assert L.ptb_gemm(1, 0, 0, 16, 16, 16, fake, 8, fake, 16, fake, 16, 0, None, 0, None) == -1  # lda < K
+    ws = B.ptb_gemm_workspace_bytes()
+    assert L.ptb_gemm(1, 0, 0, 16, 16, 16, fake, 16, fake, 16, fake, 16, 0, fake, ws - 1, None) == -3
+    assert L.ptb_gemm(1, 0, 0, 16, 16, 16, fake, 16, fake, 16, fake, 16, 0, fake + 16, ws, None) == -3
     assert L.ptb_layernorm_forward(1, 4, 12, fake, fake, fake, 1e-5, fake, fake, fake, None) == -1
     assert B.ptb_status_string(-3).startswith("workspace")

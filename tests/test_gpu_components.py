@@ -82,6 +82,41 @@ def test_gemm_layouts(dtype, a_layout, b_layout, M, N, K):
         check(f"C(c_f32={c_f32})", _host(c), ref, dtype)
 
 
+# Tile counts between one and two waves of 256 CUs, so the split (stream-K)
+# schedule runs when a workspace is given: (a) 384 tiles, each split tile
+# shared by two workers; (b) 304 tiles with ragged N and a K of 17 tiles
+# (not a multiple of the 4-tile round), so tiles have several contributors
+# and some workers get no iterations.
+SPLIT_SHAPES = [(1000, 24576, 256), (2048, 9600, 520)]
+
+
+@pytest.mark.parametrize("a_layout,b_layout", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_gemm_split_schedule(a_layout, b_layout, M, N, K):
+    print(f"gemm split layouts={a_layout}{b_layout} M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M + N + K + a_layout * 2 + b_layout)
+    code, tdt = _dt("bf16")
+    a = _rand(rng, (M, K), "bf16")
+    b = _rand(rng, (N, K), "bf16")
+    ref = a.astype(np.float64) @ b.astype(np.float64).T
+    a_store = a if a_layout == 0 else np.ascontiguousarray(a.T)
+    b_store = b if b_layout == 0 else np.ascontiguousarray(b.T)
+    ad, bd = to_device(a_store, tdt), to_device(b_store, tdt)
+    lda = K if a_layout == 0 else M
+    ldb = K if b_layout == 0 else N
+    ws = torch.empty(B.ptb_gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    for c_f32 in (0, 1):
+        outs = []
+        for rep in range(2):
+            ws.fill_(0xFF if rep else 0x00)  # stale workspace contents must not matter
+            c = torch.empty((M, N), dtype=torch.float32 if c_f32 else tdt, device="cuda")
+            B.ptb_gemm(code, a_layout, b_layout, M, N, K, ad, lda, bd, ldb, c, N, c_f32, workspace=ws)
+            outs.append(c)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), "split schedule must be deterministic"
+        check(f"C(c_f32={c_f32}, split)", _host(outs[0]), ref, "bf16")
+
+
 def _swa_case(dtype, batch, seq, H, d, w):
     rng = np.random.default_rng(batch * 1000 + seq + w + d)
     A = H * d

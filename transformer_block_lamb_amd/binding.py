@@ -21,7 +21,8 @@ STATUS = {0: "PTB_OK", -1: "PTB_ERR_INVALID_ARG", -2: "PTB_ERR_UNSUPPORTED",
 EXPORTED = ("ptb_saved_bytes", "ptb_scratch_bytes", "ptb_forward", "ptb_backward",
             "lamb_scratch_bytes", "lamb_step", "ptb_status_string",
             "ptb_forward_stage", "ptb_backward_stage",
-            "ptb_layernorm_forward", "ptb_gemm", "ptb_swa_forward", "ptb_swa_backward")
+            "ptb_layernorm_forward", "ptb_gemm_workspace_bytes", "ptb_gemm", "ptb_swa_forward",
+            "ptb_swa_backward")
 FWD_STAGES = ("layernorm", "gemm_in", "attention", "gemm_out")
 BWD_STAGES = ("gemm_dcat", "gemm_dw_out", "attention", "gemm_dw_in", "gemm_dxn", "layernorm")
 
@@ -74,8 +75,9 @@ def lib():
             "ptb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "ptb_layernorm_forward": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp,
                                                      vp]),
+            "ptb_gemm_workspace_bytes": (ctypes.c_size_t, []),
             "ptb_gemm": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64,
-                                        i32, vp]),
+                                        i32, vp, ctypes.c_size_t, vp]),
             "ptb_swa_forward": (ctypes.c_int, [pd, vp, vp, i64, vp, vp]),
             "ptb_swa_backward": (ctypes.c_int, [pd, vp, vp, i64, vp, vp, vp, vp, vp]),
         }
@@ -93,6 +95,10 @@ def _ptr(t):
     if isinstance(t, int):
         return t
     return t.data_ptr()
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
 def _stream(stream):
@@ -199,9 +205,16 @@ def ptb_layernorm_forward(dtype, rows, width, x, gamma, beta, eps, xn, mean, rst
            "ptb_layernorm_forward")
 
 
-def ptb_gemm(dtype, a_layout, b_layout, M, N, K, a, lda, b, ldb, c, ldc, c_f32=0, stream=None):
+def ptb_gemm_workspace_bytes():
+    return int(lib().ptb_gemm_workspace_bytes())
+
+
+def ptb_gemm(dtype, a_layout, b_layout, M, N, K, a, lda, b, ldb, c, ldc, c_f32=0,
+             workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else _nbytes(workspace)
     _check(lib().ptb_gemm(dtype, a_layout, b_layout, M, N, K, _ptr(a), lda, _ptr(b), ldb,
-                          _ptr(c), ldc, c_f32, _stream(stream)), "ptb_gemm")
+                          _ptr(c), ldc, c_f32, _ptr(workspace), ws_bytes, _stream(stream)),
+           "ptb_gemm")
 
 
 def ptb_swa_forward(dims, qkv, o, ldo, lse, stream=None):

@@ -58,7 +58,7 @@ struct Dims {
 // the attention scores are formed at fp32-level accuracy (see the input
 // GEMM and the attention kernels).
 struct SavedLayout {
-  size_t xn, xn_lo, qk_lo, qkv, f, cat, mean, rstd, lse, total;
+  size_t xn, xn_lo, qk_lo, qkv, f, cat, mean, rstd, lse, gemm_ws, total;
   explicit SavedLayout(const Dims& d) {
     const bool split = d.e == 2;
     size_t o = 0;
@@ -71,13 +71,14 @@ struct SavedLayout {
     mean = o; o += up(d.T * 4);
     rstd = o; o += up(d.T * 4);
     lse = o;  o += up(d.B * d.H * d.S * 4);
+    gemm_ws = o; o += split ? kGemmWsBytes : 0;  // transient, forward GEMMs only
     total = o;
   }
 };
 
 // Backward temporaries.
 struct ScratchLayout {
-  size_t d_o, dz, dxn, dvec, gpart, bpart, total;
+  size_t d_o, dz, dxn, dvec, gpart, bpart, gemm_ws, total;
   explicit ScratchLayout(const Dims& d) {
     const int64_t nblk = (d.T + ln_bwd_rows_per_block() - 1) / ln_bwd_rows_per_block();
     size_t o = 0;
@@ -87,6 +88,7 @@ struct ScratchLayout {
     dvec = o;  o += up(d.B * d.H * d.S * 4);
     gpart = o; o += up(nblk * d.h * 4);
     bpart = o; o += up(nblk * d.h * 4);
+    gemm_ws = o; o += d.e == 2 ? kGemmWsBytes : 0;
     total = o;
   }
 };
@@ -151,6 +153,8 @@ int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const 
   float* mean = at<float>(saved, L.mean);
   float* rstd = at<float>(saved, L.rstd);
   float* lse = at<float>(saved, L.lse);
+  void* ws = dt == PTB_BF16 ? at<char>(saved, L.gemm_ws) : nullptr;
+  const size_t ws_bytes = dt == PTB_BF16 ? kGemmWsBytes : 0;
   const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
                    3 * d.A, qk_lo};
   for (int s = (stage < 0 ? 0 : stage); s < (stage < 0 ? PTB_FWD_STAGES : stage + 1); ++s) {
@@ -165,6 +169,8 @@ int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const 
         GemmDesc g{(int)d.T, (int)d.N1, (int)d.h, kKContig, kKContig, xn, d.h, w_in, d.h};
         g.a2 = xn_lo;
         g.n_split = (int)(2 * d.A);
+        g.ws = ws;
+        g.ws_bytes = ws_bytes;
         e = launch_gemm_in_fwd(dt, g, qkv, qk_lo, f, cat, (int)d.A, (int)d.F, stream);
         break;
       }
@@ -172,7 +178,9 @@ int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const 
         e = launch_swa_fwd(dt, sw, cat, d.K2, lse, stream);
         break;
       case PTB_FWD_GEMM_OUT: {  // y = [x] + cat w_out
-        const GemmDesc g{(int)d.T, (int)d.h, (int)d.K2, kKContig, kMNContig, cat, d.K2, w_out, d.h};
+        GemmDesc g{(int)d.T, (int)d.h, (int)d.K2, kKContig, kMNContig, cat, d.K2, w_out, d.h};
+        g.ws = ws;
+        g.ws_bytes = ws_bytes;
         e = launch_gemm_out_fwd(dt, g, x, dims->add_residual, y, stream);
         break;
       }
@@ -218,18 +226,24 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
   float* dvec = at<float>(scratch, R.dvec);
   float* gpart = at<float>(scratch, R.gpart);
   float* bpart = at<float>(scratch, R.bpart);
+  void* ws = dt == PTB_BF16 ? at<char>(scratch, R.gemm_ws) : nullptr;
+  const size_t ws_bytes = dt == PTB_BF16 ? kGemmWsBytes : 0;
   const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
                    3 * d.A, qk_lo};
   for (int s = (stage < 0 ? 0 : stage); s < (stage < 0 ? PTB_BWD_STAGES : stage + 1); ++s) {
     hipError_t e = hipSuccess;
     switch (s) {
       case PTB_BWD_GEMM_DCAT: {  // dcat = dy w_out^T -> dO | dz[:, 3A:] = dg * GeLU'(f)
-        const GemmDesc g{(int)d.T, (int)d.K2, (int)d.h, kKContig, kKContig, dy, d.h, w_out, d.h};
+        GemmDesc g{(int)d.T, (int)d.K2, (int)d.h, kKContig, kKContig, dy, d.h, w_out, d.h};
+        g.ws = ws;
+        g.ws_bytes = ws_bytes;
         e = launch_gemm_dcat(dt, g, f, d_o, dz, (int)d.A, (int)d.F, stream);
         break;
       }
       case PTB_BWD_GEMM_DW_OUT: {  // dw_out = cat^T dy
-        const GemmDesc g{(int)d.K2, (int)d.h, (int)d.T, kMNContig, kMNContig, cat, d.K2, dy, d.h};
+        GemmDesc g{(int)d.K2, (int)d.h, (int)d.T, kMNContig, kMNContig, cat, d.K2, dy, d.h};
+        g.ws = ws;
+        g.ws_bytes = ws_bytes;
         e = launch_gemm_store(dt, g, dw_out, d.h, false, stream);
         break;
       }
@@ -237,12 +251,16 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
         e = launch_swa_bwd(dt, sw, cat, d.K2, d_o, d.A, lse, dvec, dz, d.N1, stream);
         break;
       case PTB_BWD_GEMM_DW_IN: {  // dw_in = dz^T xn
-        const GemmDesc g{(int)d.N1, (int)d.h, (int)d.T, kMNContig, kMNContig, dz, d.N1, xn, d.h};
+        GemmDesc g{(int)d.N1, (int)d.h, (int)d.T, kMNContig, kMNContig, dz, d.N1, xn, d.h};
+        g.ws = ws;
+        g.ws_bytes = ws_bytes;
         e = launch_gemm_store(dt, g, dw_in, d.h, false, stream);
         break;
       }
       case PTB_BWD_GEMM_DXN: {  // dxn = dz w_in (fp32)
-        const GemmDesc g{(int)d.T, (int)d.h, (int)d.N1, kKContig, kMNContig, dz, d.N1, w_in, d.h};
+        GemmDesc g{(int)d.T, (int)d.h, (int)d.N1, kKContig, kMNContig, dz, d.N1, w_in, d.h};
+        g.ws = ws;
+        g.ws_bytes = ws_bytes;
         e = launch_gemm_store(dt, g, dxn, d.h, true, stream);
         break;
       }
@@ -342,9 +360,11 @@ int ptb_layernorm_forward(int32_t dtype, int32_t rows, int32_t width, const void
       launch_ln_fwd(dtype, x, gamma, beta, eps, rows, width, xn, nullptr, mean, rstd, stream));
 }
 
+size_t ptb_gemm_workspace_bytes(void) { return kGemmWsBytes; }
+
 int ptb_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t M, int32_t N, int32_t K,
              const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc,
-             int32_t c_f32, hipStream_t stream) {
+             int32_t c_f32, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if ((dtype != PTB_F32 && dtype != PTB_BF16) || M < 1 || N < 1 || K < 1) return PTB_ERR_INVALID_ARG;
   if ((a_layout != 0 && a_layout != 1) || (b_layout != 0 && b_layout != 1)) return PTB_ERR_INVALID_ARG;
   if (!all_aligned({a, b, c})) return PTB_ERR_INVALID_ARG;
@@ -360,7 +380,14 @@ int ptb_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t M, int32
   } else if (c_f32 == 0) {
     c_f32 = 1;  // fp32 operands always produce fp32
   }
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+                                workspace_bytes < kGemmWsBytes))
+    return PTB_ERR_WORKSPACE;
   GemmDesc g{M, N, K, a_layout, b_layout, a, lda, b, ldb};
+  if (dtype == PTB_BF16) {
+    g.ws = workspace;
+    g.ws_bytes = workspace_bytes;
+  }
   return hip_status(launch_gemm_store(dtype, g, c, ldc, c_f32 != 0, stream));
 }
 

@@ -290,11 +290,74 @@ struct FragReader {
   }
 };
 
+// --------------------------------------------------------------- schedule
+// Logical tile order: groups of kGroupM M-tiles, M-fastest within a group.
+// The first nh N-tiles also run the a2 pass (2 nk1 K iterations instead of
+// nk1).  start(l) is the first iteration of logical tile l in the
+// concatenation of all tiles' K iterations; locate() inverts it.
+struct Sched {
+  int ntm, ntn, nk1, nh;
+  __host__ __device__ int cost(int tn) const { return tn < nh ? 2 * nk1 : nk1; }
+  __host__ __device__ int64_t col_prefix(int tn) const {
+    return (int64_t)nk1 * (tn + (tn < nh ? tn : nh));
+  }
+  __host__ __device__ int group_size(int first_m) const {
+    return ntm - first_m < kGroupM ? ntm - first_m : kGroupM;
+  }
+  __host__ __device__ void tile(int l, int& tm, int& tn) const {
+    const int group = l / (kGroupM * ntn), first_m = group * kGroupM;
+    const int gsize = group_size(first_m), in = l - group * kGroupM * ntn;
+    tn = in / gsize;
+    tm = first_m + in % gsize;
+  }
+  __host__ __device__ int64_t start(int l) const {
+    if (l >= ntm * ntn) return (int64_t)ntm * col_prefix(ntn);
+    int tm, tn;
+    tile(l, tm, tn);
+    const int first_m = tm - tm % kGroupM;
+    return (int64_t)first_m * col_prefix(ntn) + (int64_t)group_size(first_m) * col_prefix(tn) +
+           (int64_t)(tm - first_m) * cost(tn);
+  }
+  __host__ __device__ void locate(int64_t it, int& l, int& koff) const {
+    const int64_t row = col_prefix(ntn);
+    const int ngroups = (ntm + kGroupM - 1) / kGroupM;
+    int group = (int)(it / (kGroupM * row));
+    if (group >= ngroups) group = ngroups - 1;
+    const int first_m = group * kGroupM, gsize = group_size(first_m);
+    int64_t rem = it - (int64_t)first_m * row;
+    const int64_t heavy = (int64_t)gsize * 2 * nk1 * nh;
+    int tn, c;
+    if (rem < heavy) {
+      c = 2 * nk1;
+      tn = (int)(rem / ((int64_t)gsize * c));
+      rem -= (int64_t)tn * gsize * c;
+    } else {
+      c = nk1;
+      rem -= heavy;
+      const int q = (int)(rem / ((int64_t)gsize * c));
+      tn = nh + q;
+      rem -= (int64_t)q * gsize * c;
+    }
+    const int r = (int)(rem / c);
+    koff = (int)(rem - (int64_t)r * c);
+    l = group * kGroupM * ntn + tn * gsize + r;
+  }
+};
+
 // a2 (optional, same layout and leading dimension as a): output tiles whose
 // first column lies below n_split accumulate a second K pass over a2 with
 // the same B, i.e. C = (A + A2) B^T there.  The input projection uses it to
 // form q and k from the LayerNorm output split into its bf16 value and bf16
 // residual, so the attention scores do not inherit the rounding of xn.
+//
+// Two schedules.  sk == 0: workgroup b computes tile tile_coords(b) whole.
+// sk == 1 (persistent, `grid` workgroups, one per CU): the first dp_tiles
+// logical tiles are dealt out whole; the K iterations of the remaining tiles
+// are split into `grid` equal contiguous ranges (stream-K), so every CU gets
+// the same amount of work when the tile count is not a multiple of the CU
+// count.  A range that covers only part of a tile writes its fp32 partial
+// tile to ws; a second kernel sums the partials of each split tile in K
+// order and runs the epilogue, so results do not depend on timing.
 struct GemmArgs {
   const bf16_t* a;
   const bf16_t* b;
@@ -303,9 +366,34 @@ struct GemmArgs {
   int n_split;
   int64_t lda, ldb;
   uint32_t a_bytes, b_bytes;
+  Sched sc;
+  int sk, grid, dp_tiles;
+  int64_t sk_base, sk_iters;
+  float* ws;
   int use_perm;
-  int16_t perm[kMaxPerm];  // N-tile order (when use_perm)
+  int16_t perm[kMaxPerm];  // N-tile order (when use_perm, sk == 0)
 };
+constexpr int kPartialFloats = BM * BN;  // one partial tile in ws
+
+// First iteration of stream-K worker w (w == grid: end of the range);
+// rounded down to a multiple of kStages so segments are whole rounds.
+__host__ __device__ inline int64_t sk_lo(const GemmArgs& g, int w) {
+  if (w >= g.grid) return g.sk_base + g.sk_iters;
+  return g.sk_base + (((int64_t)w * g.sk_iters / g.grid) & ~(int64_t)(kStages - 1));
+}
+// The stream-K worker whose range holds iteration it.
+__device__ inline int sk_owner(const GemmArgs& g, int64_t it) {
+  int w = (int)((it - g.sk_base) * g.grid / g.sk_iters);
+  w = w < 0 ? 0 : (w > g.grid - 1 ? g.grid - 1 : w);
+  while (w > 0 && sk_lo(g, w) > it) --w;
+  while (w < g.grid - 1 && sk_lo(g, w + 1) <= it) ++w;
+  return w;
+}
+// ws slot of worker w's segment of a tile starting at iteration s: its first
+// segment (which may start inside the tile) or its last one.
+__device__ inline int sk_slot(const GemmArgs& g, int w, int64_t s) {
+  return sk_lo(g, w) >= s ? 2 * w : 2 * w + 1;
+}
 
 // 16 MFMAs of one K=16 step: the wave's 128x128 accumulators.
 __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
@@ -317,16 +405,17 @@ __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const bf16x8_t (
 }
 
 // Scheduling of one phase (masks: 0x008 MFMA, 0x020 memory read, 0x100 LDS
-// read): the 16 MFMAs, with NR LDS reads and NV memory instructions dealt
-// out after the first MFMAs, closed by a full scheduling barrier.
-template <int NR, int NV>
+// read): the 16 MFMAs, each followed by an LDS read on every RS-th one (NR in
+// all) and a memory read on every VS-th one (NV in all), closed by a full
+// scheduling barrier.
+template <int NR, int RS, int NV, int VS>
 __device__ __forceinline__ void interleave() {
-  static_assert(NR <= 16 && NV <= 16, "one of each per MFMA at most");
+  static_assert(NR * RS <= 16 && NV * VS <= 16, "fits in one phase");
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (i % RS == 0 && i / RS < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i % VS == VS - 1 && i / VS < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -343,17 +432,56 @@ __device__ __forceinline__ void wait_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Main loop: a kStages-deep LDS pipeline over K tiles t = 0, 1, ... (tiles
-// nk1.. of a two-pass tile read a2).  While tile t is multiplied, the loads
-// of tiles t+1 .. t+kStages-1 are in flight; tile t+kStages-1 is issued in
-// the first half of tile t into the stage tile t-1 used.  Each tile is two
-// phases of 16 MFMAs: the first reads the second K=16 step's fragments and
-// issues the loads, then each wave waits for its own loads of tile t+1 and
-// the workgroup meets at the single barrier of the tile; the second phase
-// reads tile t+1's first fragments.  Tiles past the end load zeros (no
-// memory traffic), so the body has no branches; the loop is unrolled by the
-// number of stages so every LDS address is static (K is padded with zero
-// tiles to whole rounds).
+// Epilogue of one row of four 32x32 accumulator blocks (a = acc[i][0..3]):
+// each wave stages its 32x128 strip in its own LDS area (fp32; block j at
+// word j*kStageBlk + {0,4,32,36}[j] so the row-chunk reads of the four
+// blocks fall on different banks) with a short fully unrolled loop, then
+// re-reads it as 8-column row chunks (4 rows x 128 columns per wave
+// instruction) and runs the epilogue in a rolled loop, so every lane issues
+// 16-byte stores.  Contains two workgroup barriers.
+constexpr int kStageRow = 36, kStageBlk = 1216;
+template <class Epi>
+__device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[4], float* stage, int row0,
+                                               int col0, int lane, int M, int N, const Epi& epi) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float* blk = stage + j * kStageBlk + (j & 1) * 4 + (j >> 1) * 32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) blk[mfma32_row(r, lane) * kStageRow + (lane & 31)] = a[j][r];
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int c = lane; c < 32 * 16; c += 64) {
+    const int rr = c >> 4, jc = c & 15, j = jc >> 2, c8 = (jc & 3) * 8;
+    const float* src = stage + j * kStageBlk + (j & 1) * 4 + (j >> 1) * 32 + rr * kStageRow + c8;
+    const float4 lo = *reinterpret_cast<const float4*>(src);
+    const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+    const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const int row = row0 + rr, col = col0 + j * 32 + c8;
+    if (row < M && col < N) epi.store8(row, col, v, N);
+  }
+  __syncthreads();
+}
+
+// Offset (floats) of this lane's accumulators acc[i][j][4 r4 .. 4 r4 + 3] in
+// a partial tile: one 1 KB run per (wave, i, j, r4), so each store or load
+// instruction of a wave is contiguous.
+__device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int lane) {
+  return ((((wave * 4 + i) * 4 + j) * 4 + r4) * 64 + lane) * 4;
+}
+
+// Main loop of one segment (K iterations kb .. ke of a tile): a kStages-deep
+// LDS pipeline over K tiles t (tiles nk1.. of a two-pass tile read a2).
+// While tile t is multiplied, the loads of tiles t+1 .. t+kStages-1 are in
+// flight; tile t+kStages-1 is issued during tile t (A in its first half, B in
+// its second) into the stage tile t-1 used.  Each tile is two phases of 16
+// MFMAs: the first reads the second K=16 step's fragments, then each wave
+// waits for its own loads of tile t+1 and the workgroup meets at the single
+// barrier of the tile; the second reads tile t+1's first fragments.  Tiles
+// past ke load zeros (no memory traffic), so the body has no branches; the
+// loop is unrolled by the number of stages so every LDS address is static,
+// and runs whole rounds of kStages tiles (an exit inside a round makes the
+// accumulators live across several loop exits, which spills them).
 template <int ALAY, int BLAY, class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
   // one array per stage, so the compiler sees that loads into one stage do
@@ -363,104 +491,177 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
   static_assert(kStages == 4, "stage arrays");
-  const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, ntm, ntn, g.use_perm ? g.perm : nullptr, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  static_assert(4 * kStageBlk * 4 <= kStageBytes, "epilogue staging");
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, g.a_bytes);
   const __amdgpu_buffer_rsrc_t ra2 = make_rsrc(g.a2 != nullptr ? g.a2 : g.a, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, g.b_bytes);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  DmaOperand<ALAY> da;
-  DmaOperand<BLAY> db;
-  da.init(wave, lane, m0, g.M, g.lda);
-  db.init(wave, lane, n0, g.N, g.ldb);
   FragReader<ALAY> fra;
   FragReader<BLAY> frb;
   fra.init(lane, wm);
   frb.init(lane, wn);
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk1 = (g.K + BK - 1) / BK;
-  const int nk = (g.a2 != nullptr && n0 < g.n_split) ? 2 * nk1 : nk1;
-  auto issue = [&](char* st, int t) {
-    const bool second = t >= nk1;
-    const int kt = second ? t - nk1 : t;
-    const int klim = t < nk ? g.K : 0;
-    da.issue(second ? ra2 : ra, st, wave, kt, klim);
-    db.issue(rb, st + kOpBytes, wave, kt, klim);
-  };
-  constexpr int kReads = (ALAY == kKContig ? 4 : 8) + (BLAY == kKContig ? 4 : 8);
-  bf16x8_t fa[2][4], fb[2][4];
-  auto tile = [&](const char* cur, const char* nxt, char* dst, int t) {
-    fra.read(fa[1], cur, 1);
-    frb.read(fb[1], cur + kOpBytes, 1);
-    issue(dst, t + kStages - 1);
-    mma_step(acc, fa[0], fb[0]);
-    interleave<kReads, kDmaPerTile>();
-    wait_barrier<(kStages - 2) * kDmaPerTile>();
-    fra.read(fa[0], nxt, 0);
-    frb.read(fb[0], nxt + kOpBytes, 0);
-    mma_step(acc, fa[1], fb[1]);
-    interleave<kReads, 0>();
-  };
-
-  issue(st0, 0);
-  issue(st1, 1);
-  issue(st2, 2);
-  wait_barrier<(kStages - 2) * kDmaPerTile>();
-  fra.read(fa[0], st0, 0);
-  frb.read(fb[0], st0 + kOpBytes, 0);
-  // whole rounds of kStages tiles (an exit inside a round makes the
-  // accumulators live across several loop exits, which spills them); the
-  // padding tiles load zeros and add nothing
-  for (int kt = 0; kt < nk; kt += kStages) {
-    tile(st0, st1, st3, kt);
-    tile(st1, st2, st0, kt + 1);
-    tile(st2, st3, st1, kt + 2);
-    tile(st3, st0, st2, kt + 3);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS
-  __syncthreads();
-
-  // Epilogue, one row of four 32x32 accumulator blocks at a time: each wave
-  // stages its 32x128 strip in its own LDS area (fp32; block j at word
-  // j*kStageBlk + {0,4,32,36}[j] so the row-chunk reads of the four blocks
-  // fall on different banks) with a short fully unrolled loop, then re-reads
-  // it as 8-column row chunks (4 rows x 128 columns per wave instruction) and
-  // runs the epilogue in a rolled loop, so every lane issues 16-byte stores.
-  constexpr int kStageRow = 36, kStageBlk = 1216;
-  static_assert(4 * kStageBlk * 4 <= kStageBytes, "epilogue staging");
   float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float* blk = stage + j * kStageBlk + (j & 1) * 4 + (j >> 1) * 32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) blk[mfma32_row(r, lane) * kStageRow + (lane & 31)] = acc[i][j][r];
+  constexpr int kReads = (ALAY == kKContig ? 4 : 8) + (BLAY == kKContig ? 4 : 8);
+  const int nk1 = g.sc.nk1;
+
+  // segment source: whole tiles first, then (sk) this worker's range
+  const int b = blockIdx.x, per = g.grid >> 3;
+  const int gl = (b & 7) * per + (b >> 3);  // sk: XCD-contiguous worker index
+  int dp_left = g.sk ? g.dp_tiles / g.grid : 1;
+  int dp_next = (b & 7) * (g.dp_tiles >> 3) + (b >> 3);
+  int64_t it = g.sk ? sk_lo(g, gl) : 0;
+  const int64_t it_end = g.sk ? sk_lo(g, gl + 1) : 0;
+  bool first_sk = true;
+  for (;;) {
+    int tm, tn, kb, ke, slot = -1;
+    if (dp_left > 0) {
+      if (g.sk) {
+        g.sc.tile(dp_next, tm, tn);
+        dp_next += per;
+      } else {
+        tile_coords(b, g.sc.ntm, g.sc.ntn, g.use_perm ? g.perm : nullptr, tm, tn);
+      }
+      --dp_left;
+      kb = 0;
+      ke = g.sc.cost(tn);
+    } else if (it < it_end) {
+      int l, koff;
+      g.sc.locate(it, l, koff);
+      g.sc.tile(l, tm, tn);
+      const int c = g.sc.cost(tn);
+      const int seg = (int)(it_end - it < (int64_t)(c - koff) ? it_end - it : (int64_t)(c - koff));
+      kb = koff;
+      ke = koff + seg;
+      if (kb > 0 || ke < c) slot = first_sk ? 2 * gl : 2 * gl + 1;
+      first_sk = false;
+      it += seg;
+    } else {
+      break;
     }
-    __syncthreads();
-#pragma unroll 1
-    for (int c = lane; c < 32 * 16; c += 64) {
-      const int rr = c >> 4, jc = c & 15, j = jc >> 2, c8 = (jc & 3) * 8;
-      const float* src = stage + j * kStageBlk + (j & 1) * 4 + (j >> 1) * 32 + rr * kStageRow + c8;
-      const float4 lo = *reinterpret_cast<const float4*>(src);
-      const float4 hi = *reinterpret_cast<const float4*>(src + 4);
-      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      const int row = m0 + wm * 128 + i * 32 + rr;
-      const int col = n0 + wn * 128 + j * 32 + c8;
-      if (row < g.M && col < g.N) epi.store8(row, col, v, g.N);
+    const int m0 = tm * BM, n0 = tn * BN;
+    DmaOperand<ALAY> da;
+    DmaOperand<BLAY> db;
+    da.init(wave, lane, m0, g.M, g.lda);
+    db.init(wave, lane, n0, g.N, g.ldb);
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    auto issue_a = [&](char* st, int t) {
+      const bool second = t >= nk1;
+      da.issue(second ? ra2 : ra, st, wave, second ? t - nk1 : t, t < ke ? g.K : 0);
+    };
+    auto issue_b = [&](char* st, int t) {
+      db.issue(rb, st + kOpBytes, wave, t >= nk1 ? t - nk1 : t, t < ke ? g.K : 0);
+    };
+    bf16x8_t fa[2][4], fb[2][4];
+    auto tile = [&](const char* cur, const char* nxt, char* dst, int t) {
+      fra.read(fa[1], cur, 1);
+      frb.read(fb[1], cur + kOpBytes, 1);
+      issue_a(dst, t + kStages - 1);
+      mma_step(acc, fa[0], fb[0]);
+      interleave<kReads, 16 / kReads, kDmaPerOp, 4>();
+      // outstanding after tile t+1's loads: tile t+2 (all) and t+3's A half
+      wait_barrier<(kStages - 3) * kDmaPerTile + kDmaPerOp>();
+      fra.read(fa[0], nxt, 0);
+      frb.read(fb[0], nxt + kOpBytes, 0);
+      issue_b(dst, t + kStages - 1);
+      mma_step(acc, fa[1], fb[1]);
+      interleave<kReads, 16 / kReads, kDmaPerOp, 4>();
+    };
+
+    issue_a(st0, kb);
+    issue_b(st0, kb);
+    issue_a(st1, kb + 1);
+    issue_b(st1, kb + 1);
+    issue_a(st2, kb + 2);
+    issue_b(st2, kb + 2);
+    wait_barrier<(kStages - 2) * kDmaPerTile>();
+    fra.read(fa[0], st0, 0);
+    frb.read(fb[0], st0 + kOpBytes, 0);
+    for (int t = kb; t < ke; t += kStages) {
+      tile(st0, st1, st3, t);
+      tile(st1, st2, st0, t + 1);
+      tile(st2, st3, st1, t + 2);
+      tile(st3, st0, st2, t + 3);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS
     __syncthreads();
+
+    if (slot < 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        epilogue_strip(acc[i], stage, m0 + wm * 128 + i * 32, n0 + wn * 128, lane, g.M, g.N, epi);
+    } else {
+      float* p = g.ws + (size_t)slot * kPartialFloats;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<float4*>(p + partial_off(wave, i, j, r4, lane)) =
+                make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                            acc[i][j][4 * r4 + 3]);
+    }
   }
+}
+
+// Stream-K fixup: one workgroup per 64-row strip (accumulator row i) of each
+// tile of the split part; a tile whose iterations several workers shared
+// gets the sum of their partials, added in worker (= K) order, and the
+// epilogue.  Two partials at a time are loaded before either is added, so
+// their loads are in flight together.
+template <class Epi>
+__global__ __launch_bounds__(kGemmThreads) void gemm_fixup_kernel(GemmArgs g, Epi epi) {
+  __shared__ __attribute__((aligned(16))) float stage_all[4][4 * kStageBlk];
+  const int l = g.dp_tiles + (blockIdx.x >> 2), i = blockIdx.x & 3;
+  const int64_t s = g.sc.start(l), e = g.sc.start(l + 1);
+  const int w0 = sk_owner(g, s), w1 = sk_owner(g, e - 1);
+  if (w0 == w1) return;  // one worker computed the whole tile
+  int tm, tn;
+  g.sc.tile(l, tm, tn);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16_t a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[j][r] = 0.f;
+#pragma unroll 1
+  for (int w = w0; w <= w1;) {
+    // the next (up to) two non-empty contributors, in order
+    const float* src[2];
+    int n = 0;
+    for (; w <= w1 && n < 2; ++w)
+      if (sk_lo(g, w) != sk_lo(g, w + 1)) src[n++] = g.ws + (size_t)sk_slot(g, w, s) * kPartialFloats;
+    float4 v[2][16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (q < n)
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          v[q][c] = *reinterpret_cast<const float4*>(src[q] + partial_off(wave, i, c >> 2, c & 3, lane));
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (q < n)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          f32x16_t& t = a[c >> 2];
+          const int r = 4 * (c & 3);
+          t[r] += v[q][c].x;
+          t[r + 1] += v[q][c].y;
+          t[r + 2] += v[q][c].z;
+          t[r + 3] += v[q][c].w;
+        }
+  }
+  epilogue_strip(a, stage_all[wave], tm * BM + wm * 128 + i * 32, tn * BN + wn * 128, lane, g.M,
+                 g.N, epi);
 }
 
 // --------------------------------------------------------------- fp32 SIMT
@@ -523,6 +724,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 g, Epi epi) {
 }
 
 // --------------------------------------------------------------- dispatch
+// Workgroups of a persistent launch: the CU count of the current device,
+// rounded down to a multiple of the 8 XCDs, at most kSkMaxGrid (0 if unknown).
+int persistent_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cus = (cus < kSkMaxGrid ? cus : kSkMaxGrid) & ~7;
+    cached[dev] = cus > 0 ? cus : -1;
+  }
+  return cached[dev] > 0 ? cached[dev] : 0;
+}
+
 template <int AL, int BL, class Epi>
 hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
   GemmArgs g;
@@ -530,21 +747,6 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
   g.b = static_cast<const bf16_t*>(d.b);
   g.a2 = static_cast<const bf16_t*>(d.a2);
   g.n_split = d.n_split;
-  // Spread the N tiles that run a second K pass evenly over the tile order
-  // (heavy tile j at slot floor((2j+1) ntn / 2 nh), light tiles fill the rest).
-  const int ntn = (d.N + BN - 1) / BN;
-  const int nh = d.a2 != nullptr ? min(ntn, (d.n_split + BN - 1) / BN) : 0;
-  g.use_perm = (nh > 0 && nh < ntn && ntn <= kMaxPerm) ? 1 : 0;
-  if (g.use_perm) {
-    int next_light = nh, j = 0;
-    for (int slot = 0; slot < ntn; ++slot) {
-      if (j < nh && slot == (int)(((int64_t)(2 * j + 1) * ntn) / (2 * nh))) {
-        g.perm[slot] = (int16_t)j++;
-      } else {
-        g.perm[slot] = (int16_t)next_light++;
-      }
-    }
-  }
   g.M = d.M; g.N = d.N; g.K = d.K; g.lda = d.lda; g.ldb = d.ldb;
   const int64_t a_elems = AL == kKContig ? (int64_t)(d.M - 1) * d.lda + d.K
                                          : (int64_t)(d.K - 1) * d.lda + d.M;
@@ -552,9 +754,58 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
                                          : (int64_t)(d.K - 1) * d.ldb + d.N;
   g.a_bytes = (uint32_t)(a_elems * 2);
   g.b_bytes = (uint32_t)(b_elems * 2);
-  const int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, Epi>), dim3(tiles), dim3(kGemmThreads), 0, s, g,
+  const int ntm = (d.M + BM - 1) / BM, ntn = (d.N + BN - 1) / BN;
+  const int nh = d.a2 != nullptr ? min(ntn, (d.n_split + BN - 1) / BN) : 0;
+  g.sc = Sched{ntm, ntn, (d.K + BK - 1) / BK, nh};
+  const int tiles = ntm * ntn;
+  g.ws = static_cast<float*>(d.ws);
+  g.use_perm = 0;
+  g.sk = 0;
+  g.grid = 8;
+  g.dp_tiles = 0;
+  g.sk_base = g.sk_iters = 0;
+
+  // Stream-K when whole tiles per CU would leave more than a tenth of the
+  // machine idle: compare the ideal share of K iterations per CU with the
+  // busiest CU of the one-tile-per-workgroup schedule (a two-pass tile
+  // counts twice).
+  const int G = persistent_grid();
+  const int64_t total = g.sc.start(tiles);
+  if (G >= 8 && g.ws != nullptr && d.ws_bytes >= kGemmWsBytes && total >= 2 * (int64_t)G * kStages) {
+    const int64_t units = tiles + (int64_t)nh * ntm;  // in light-tile units
+    const int64_t dp_time = ((units + G - 1) / G) * g.sc.nk1;
+    if ((double)total / G < 0.9 * (double)dp_time) {
+      g.sk = 1;
+      g.grid = G;
+      g.dp_tiles = nh == 0 ? (tiles / G) * G : 0;
+      g.sk_base = g.sc.start(g.dp_tiles);
+      g.sk_iters = total - g.sk_base;
+    }
+  }
+  if (!g.sk) {
+    // Spread the N tiles that run a second K pass evenly over the tile order
+    // (heavy tile j at slot floor((2j+1) ntn / 2 nh), light tiles fill the rest).
+    g.use_perm = (nh > 0 && nh < ntn && ntn <= kMaxPerm) ? 1 : 0;
+    if (g.use_perm) {
+      int next_light = nh, j = 0;
+      for (int slot = 0; slot < ntn; ++slot) {
+        if (j < nh && slot == (int)(((int64_t)(2 * j + 1) * ntn) / (2 * nh))) {
+          g.perm[slot] = (int16_t)j++;
+        } else {
+          g.perm[slot] = (int16_t)next_light++;
+        }
+      }
+    }
+    hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, Epi>), dim3(tiles), dim3(kGemmThreads), 0, s, g,
+                       epi);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, Epi>), dim3(g.grid), dim3(kGemmThreads), 0, s, g,
                      epi);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((gemm_fixup_kernel<Epi>), dim3(4 * (tiles - g.dp_tiles)), dim3(kGemmThreads), 0,
+                     s, g, epi);
   return hipGetLastError();
 }
 

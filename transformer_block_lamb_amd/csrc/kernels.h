@@ -22,7 +22,15 @@ struct GemmDesc {
   // over a2 (same layout as a), i.e. C = (A + A2) B^T there.
   const void* a2 = nullptr;
   int n_split = 0;
+  // bf16 only: workspace for split (stream-K) schedules; may be null, then
+  // every workgroup computes whole tiles.  Needs kGemmWsBytes.
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
 };
+// Stream-K: at most kSkMaxGrid persistent workgroups, each with two fp32
+// 256 x 256 partial tiles in the workspace.
+constexpr int kSkMaxGrid = 256;
+constexpr size_t kGemmWsBytes = (size_t)2 * kSkMaxGrid * 256 * 256 * 4;
 
 // ---- layernorm.hip
 // xn_lo (bf16 only, may be null): receives xn - bf16(xn) rounded to bf16.
