@@ -11,10 +11,10 @@
 //
 // bf16 path (gfx950 MFMA): 256x256 output tile per workgroup of 4 waves, each
 // wave a 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks with fp32
-// accumulators (all 256 AGPRs); K step 32.  Operand tiles go from memory
+// accumulators (all 256 AGPRs); K step 64.  Operand tiles go from memory
 // straight into LDS (buffer loads with the LDS bit, no register staging)
-// through a 4-stage ring, so three K tiles of loads are in flight while one
-// is multiplied.  M/N-contiguous operands stay in that layout in LDS and are
+// through a 2-stage ring: the loads of the next K tile are in flight for a
+// whole tile of MFMAs.  M/N-contiguous operands stay in that layout in LDS and are
 // read with the transposing LDS read (ds_read_b64_tr_b16) into the K-major
 // MFMA fragments.  Edges are masked by the buffer unit's range check (zero
 // fill), so any M, N, K is accepted.
@@ -32,9 +32,9 @@
 namespace ptb {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int kStages = 4;                    // K tiles resident in LDS
-constexpr int kOpBytes = BM * BK * 2;         // one operand tile, 16 KB
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kStages = 2;                    // K tiles resident in LDS (2 x 64 KB)
+constexpr int kOpBytes = BM * BK * 2;         // one operand tile, 32 KB
 constexpr int kStageBytes = 2 * kOpBytes;     // A tile, then B tile
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;
@@ -197,16 +197,17 @@ __device__ __forceinline__ void tile_coords(int bid, int ntm, int ntn, const int
 }
 
 // --------------------------------------------------------------- bf16 operand tiles
-// One operand tile is 256 rows (of M or N) x 32 of K, 16 KB, and reaches LDS
+// One operand tile is 256 rows (of M or N) x 64 of K, 32 KB, and reaches LDS
 // by direct buffer->LDS loads (buffer_load_dwordx4 ... lds): one wave
 // instruction writes 1 KB of LDS, lane L's 16 bytes at byte 16 L, so the LDS
 // layout is chosen by which global piece each lane fetches.  Out-of-range
 // lanes (rows past M/N, K past the end) are steered outside the buffer and
 // the load then writes zeros.
 //
-//   K-contiguous operand: LDS row r (64 bytes) holds the 32 K values of tile
-//   row r as four 16-byte slots; logical slot c sits at slot c ^ ((r>>2)&3),
-//   so the 16-byte fragment reads of 16 consecutive rows hit all 64 banks.
+//   K-contiguous operand: LDS row r (128 bytes, a whole cache line of the
+//   source row) holds the 64 K values of tile row r as eight 16-byte slots;
+//   logical slot c sits at slot c ^ ((r>>1)&7), so the 16-byte fragment
+//   reads of 16 consecutive rows hit all 64 banks.
 //   M/N-contiguous operand: LDS row k (512 bytes) holds tile K row k; its 16
 //   32-byte pairs (16 M/N values each) are permuted, logical pair P at
 //   P ^ (2 (k&3)), so the transposing fragment reads (ds_read_b64_tr_b16,
@@ -228,8 +229,8 @@ struct DmaOperand {
       const int chunk = i * 4 + wave;  // 1 KB of LDS
       int row, kk;
       if (LAY == kKContig) {
-        row = 16 * chunk + (lane >> 2);
-        kk = 8 * ((lane & 3) ^ (lane >> 4));
+        row = 8 * chunk + (lane >> 3);
+        kk = 8 * ((lane & 7) ^ ((row >> 1) & 7));
         base[i] = (uint32_t)(((int64_t)(r0 + row) * ld + kk) * 2);
       } else {
         kk = 2 * chunk + (lane >> 5);
@@ -261,9 +262,9 @@ struct FragReader {
   __device__ __forceinline__ void init(int lane, int wsel) {
     if (LAY == kKContig) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        off[ks] = (wsel * 128 + (lane & 31)) * 64 +
-                  16 * ((2 * ks + (lane >> 5)) ^ ((lane >> 2) & 3));
+      for (int ks = 0; ks < 4; ++ks)
+        off[ks] = (wsel * 128 + (lane & 31)) * 128 +
+                  16 * ((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7));
     } else {
       // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
       // element i%4 of the 4-value pieces addressed by lanes 4e + i/4
@@ -279,7 +280,7 @@ struct FragReader {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (LAY == kKContig) {
-        f[i] = *reinterpret_cast<const bf16x8_t*>(op + off[ks] + i * 2048);
+        f[i] = *reinterpret_cast<const bf16x8_t*>(op + off[ks] + i * 4096);
       } else {
         const char* p = op + off[i] + ks * 8192;
         const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)p);
@@ -470,27 +471,26 @@ __device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int l
   return ((((wave * 4 + i) * 4 + j) * 4 + r4) * 64 + lane) * 4;
 }
 
-// Main loop of one segment (K iterations kb .. ke of a tile): a kStages-deep
+// Main loop of one segment (K iterations kb .. ke of a tile): a two-stage
 // LDS pipeline over K tiles t (tiles nk1.. of a two-pass tile read a2).
-// While tile t is multiplied, the loads of tiles t+1 .. t+kStages-1 are in
-// flight; tile t+kStages-1 is issued during tile t (A in its first half, B in
-// its second) into the stage tile t-1 used.  Each tile is two phases of 16
-// MFMAs: the first reads the second K=16 step's fragments, then each wave
-// waits for its own loads of tile t+1 and the workgroup meets at the single
-// barrier of the tile; the second reads tile t+1's first fragments.  Tiles
-// past ke load zeros (no memory traffic), so the body has no branches; the
-// loop is unrolled by the number of stages so every LDS address is static,
-// and runs whole rounds of kStages tiles (an exit inside a round makes the
-// accumulators live across several loop exits, which spills them).
+// Each tile is four phases of 16 MFMAs (one K=16 step each); every phase
+// reads the next step's fragments while it multiplies.  After the third
+// phase each wave waits for its own loads of tile t+1 and the workgroup
+// meets at the single barrier of the tile: from then on tile t's stage is
+// free, so the fourth phase reads tile t+1's first fragments and issues the
+// loads of tile t+2 into tile t's stage, a whole tile ahead of their use.
+// Tiles past ke load zeros (no memory traffic), so the body has no
+// branches; the loop is unrolled by the number of stages so every LDS
+// address is static, and runs whole rounds of kStages tiles (an exit inside
+// a round makes the accumulators live across several loop exits, which
+// spills them).
 template <int ALAY, int BLAY, class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
   // one array per stage, so the compiler sees that loads into one stage do
   // not alias fragment reads from another
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
-  static_assert(kStages == 4, "stage arrays");
+  static_assert(kStages == 2, "stage arrays");
   static_assert(4 * kStageBlk * 4 <= kStageBytes, "epilogue staging");
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, g.a_bytes);
   const __amdgpu_buffer_rsrc_t ra2 = make_rsrc(g.a2 != nullptr ? g.a2 : g.a, g.a_bytes);
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   FragReader<BLAY> frb;
   fra.init(lane, wm);
   frb.init(lane, wn);
-  float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
+  float* stage = reinterpret_cast<float*>((wave < 2 ? st0 : st1) + (wave & 1) * (kStageBytes / 2));
   constexpr int kReads = (ALAY == kKContig ? 4 : 8) + (BLAY == kKContig ? 4 : 8);
   const int nk1 = g.sc.nk1;
 
@@ -560,35 +560,39 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       db.issue(rb, st + kOpBytes, wave, t >= nk1 ? t - nk1 : t, t < ke ? g.K : 0);
     };
     bf16x8_t fa[2][4], fb[2][4];
-    auto tile = [&](const char* cur, const char* nxt, char* dst, int t) {
+    auto tile = [&](char* cur, const char* nxt, int t) {
       fra.read(fa[1], cur, 1);
       frb.read(fb[1], cur + kOpBytes, 1);
-      issue_a(dst, t + kStages - 1);
       mma_step(acc, fa[0], fb[0]);
-      interleave<kReads, 16 / kReads, kDmaPerOp, 4>();
-      // outstanding after tile t+1's loads: tile t+2 (all) and t+3's A half
-      wait_barrier<(kStages - 3) * kDmaPerTile + kDmaPerOp>();
+      interleave<kReads, 16 / kReads, 0, 1>();
+      fra.read(fa[0], cur, 2);
+      frb.read(fb[0], cur + kOpBytes, 2);
+      mma_step(acc, fa[1], fb[1]);
+      interleave<kReads, 16 / kReads, 0, 1>();
+      fra.read(fa[1], cur, 3);
+      frb.read(fb[1], cur + kOpBytes, 3);
+      mma_step(acc, fa[0], fb[0]);
+      interleave<kReads, 16 / kReads, 0, 1>();
+      // tile t+1 has landed and every wave is done reading tile t
+      wait_barrier<0>();
       fra.read(fa[0], nxt, 0);
       frb.read(fb[0], nxt + kOpBytes, 0);
-      issue_b(dst, t + kStages - 1);
+      issue_a(cur, t + 2);
+      issue_b(cur, t + 2);
       mma_step(acc, fa[1], fb[1]);
-      interleave<kReads, 16 / kReads, kDmaPerOp, 4>();
+      interleave<kReads, 16 / kReads, kDmaPerTile, 1>();
     };
 
     issue_a(st0, kb);
     issue_b(st0, kb);
     issue_a(st1, kb + 1);
     issue_b(st1, kb + 1);
-    issue_a(st2, kb + 2);
-    issue_b(st2, kb + 2);
-    wait_barrier<(kStages - 2) * kDmaPerTile>();
+    wait_barrier<kDmaPerTile>();
     fra.read(fa[0], st0, 0);
     frb.read(fb[0], st0 + kOpBytes, 0);
     for (int t = kb; t < ke; t += kStages) {
-      tile(st0, st1, st3, t);
-      tile(st1, st2, st0, t + 1);
-      tile(st2, st3, st1, t + 2);
-      tile(st3, st0, st2, t + 3);
+      tile(st0, st1, t);
+      tile(st1, st0, t + 1);
     }
     __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS
     __syncthreads();
