@@ -16,8 +16,10 @@
 //            forward                                      (+2 bytes/param)
 // All tensors of a call share one launch per pass (a kernel-argument table
 // of up to 16 tensors; a workgroup finds its tensor from the block ranges).
-// Each thread moves 16-byte vectors (4 fp32) and keeps 8 of them in flight
-// per array.
+// Each thread moves 16-byte vectors (4 fp32) and keeps 4 of them in flight
+// per array.  Every stream is touched once per pass, so loads and stores
+// carry the non-temporal hint (measured on this access mix: about 5.3 TB/s
+// without it, 5.7-6.0 TB/s with it).
 #include "common.h"
 #include "kernels.h"
 
@@ -25,8 +27,26 @@ namespace ptb {
 namespace {
 
 constexpr int kLambThreads = 256;
-constexpr int kLambUnroll = 8;
+constexpr int kLambUnroll = 4;
 constexpr int kLambChunk = kLambThreads * 4 * kLambUnroll;  // elements per workgroup
+
+__device__ __forceinline__ float4 ld_nt(const float* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_nt(float* p, float4 v) {
+  const f32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
+}
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld_nt(const bf16_t* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st_nt(bf16_t* p, uint2 v) {
+  const u32x2_t t = {v.x, v.y};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t*>(p));
+}
 
 __device__ __forceinline__ int find_tensor(const LambBatch& b, int blk) {
   int t = 0;
@@ -39,7 +59,7 @@ __device__ __forceinline__ int find_tensor(const LambBatch& b, int blk) {
 template <typename G> struct GradLoad;
 template <> struct GradLoad<bf16_t> {
   static __device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
-    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p) + i);
+    const uint2 u = ld_nt(static_cast<const bf16_t*>(p) + i);
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
   }
@@ -49,7 +69,7 @@ template <> struct GradLoad<bf16_t> {
 };
 template <> struct GradLoad<float> {
   static __device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
-    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    return ld_nt(static_cast<const float*>(p) + i);
   }
   static __device__ __forceinline__ float ld1(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
@@ -81,9 +101,9 @@ __device__ __forceinline__ void pass_a_chunk(const LambBatch& b, const LambHyper
 #pragma unroll
     for (int u = 0; u < kLambUnroll; ++u) {
       const int64_t i = base + (int64_t)(u * kLambThreads + threadIdx.x) * 4;
-      wv[u] = *reinterpret_cast<const float4*>(w + i);
-      mv[u] = *reinterpret_cast<const float4*>(m + i);
-      vv[u] = *reinterpret_cast<const float4*>(v + i);
+      wv[u] = ld_nt(w + i);
+      mv[u] = ld_nt(m + i);
+      vv[u] = ld_nt(v + i);
       gv[u] = GradLoad<G>::ld4(g, i);
     }
 #pragma unroll
@@ -101,8 +121,8 @@ __device__ __forceinline__ void pass_a_chunk(const LambBatch& b, const LambHyper
         sw += ww[e] * ww[e];
         su += uu * uu;
       }
-      *reinterpret_cast<float4*>(m + i) = make_float4(mm[0], mm[1], mm[2], mm[3]);
-      *reinterpret_cast<float4*>(v + i) = make_float4(vs[0], vs[1], vs[2], vs[3]);
+      st_nt(m + i, make_float4(mm[0], mm[1], mm[2], mm[3]));
+      st_nt(v + i, make_float4(vs[0], vs[1], vs[2], vs[3]));
     }
   } else {
     for (int64_t i = base + threadIdx.x; i < min(n, base + kLambChunk); i += kLambThreads) {
@@ -188,9 +208,9 @@ __global__ __launch_bounds__(kLambThreads) void lamb_pass_b(LambBatch b, LambHyp
 #pragma unroll
     for (int u = 0; u < kLambUnroll; ++u) {
       const int64_t i = base + (int64_t)(u * kLambThreads + threadIdx.x) * 4;
-      wv[u] = *reinterpret_cast<const float4*>(w + i);
-      mv[u] = *reinterpret_cast<const float4*>(m + i);
-      vv[u] = *reinterpret_cast<const float4*>(v + i);
+      wv[u] = ld_nt(w + i);
+      mv[u] = ld_nt(m + i);
+      vv[u] = ld_nt(v + i);
     }
 #pragma unroll
     for (int u = 0; u < kLambUnroll; ++u) {
@@ -200,9 +220,8 @@ __global__ __launch_bounds__(kLambThreads) void lamb_pass_b(LambBatch b, LambHyp
       o.y = wv[u].y - step * lamb_u(wv[u].y, mv[u].y, vv[u].y, wd, hp);
       o.z = wv[u].z - step * lamb_u(wv[u].z, mv[u].z, vv[u].z, wd, hp);
       o.w = wv[u].w - step * lamb_u(wv[u].w, mv[u].w, vv[u].w, wd, hp);
-      *reinterpret_cast<float4*>(w + i) = o;
-      if (wc != nullptr)
-        *reinterpret_cast<uint2*>(wc + i) = make_uint2(pack_bf2(o.x, o.y), pack_bf2(o.z, o.w));
+      st_nt(w + i, o);
+      if (wc != nullptr) st_nt(wc + i, make_uint2(pack_bf2(o.x, o.y), pack_bf2(o.z, o.w)));
     }
   } else {
     for (int64_t i = base + threadIdx.x; i < min(n, base + kLambChunk); i += kLambThreads) {
