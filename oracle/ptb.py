@@ -224,13 +224,74 @@ def ptb_forward_branches(dims, x, gamma, beta, w_in, w_out):
 def serial_forward(dims, x, gamma, beta, w_in, w_out, gamma2=None, beta2=None):
     """The serial pre-LN block the PTB replaces, for contrast in tests:
     h = x + Attention(LN1(x)); y = h + MLP(LN2(h))."""
-    x = _f64(x)
     g2 = gamma if gamma2 is None else gamma2
     b2 = beta if beta2 is None else beta2
-    xn, _, _, _ = layernorm(x, gamma, beta, dims["ln_eps"])
-    hid = x + attn_branch(dims, xn, w_in, w_out)
-    hn, _, _, _ = layernorm(hid, g2, b2, dims["ln_eps"])
-    return hid + mlp_branch(dims, hn, w_in, w_out)
+    y, _ = serial_block_forward(dims, x, gamma, beta, g2, b2, w_in, w_out)
+    return y
+
+
+# --------------------------------------------------------------------------
+# The serial pre-LN block (the arrangement the PTB row replaces)
+# --------------------------------------------------------------------------
+# The page writes the serial block as y = x + MLP(LN(x + Attention(LN(x)))),
+# which drops the residual around the attention sub-layer; the block the PTB
+# row contrasts with is the usual pre-LN transformer layer, read here as
+#   h = x + Attention(LN1(x)),   y = h + MLP(LN2(h)),
+# with its own (gamma, beta) per LayerNorm and the same projections as the
+# PTB: w_in rows Q | K | V | FC1, w_out rows attention-out | FC2.  Both
+# residuals are always present (LN2 needs the whole h, so the serial block is
+# not a sum of per-branch partials).
+def serial_block_forward(dims, x, gamma1, beta1, gamma2, beta2, w_in, w_out):
+    """Returns y and the intermediates its backward uses."""
+    _, _, _, _, A, _ = _split(dims)
+    x, w_in, w_out = _f64(x), _f64(w_in), _f64(w_out)
+    xn1, xhat1, _, rstd1 = layernorm(x, gamma1, beta1, dims["ln_eps"])
+    q = xn1 @ w_in[0:A].T
+    k = xn1 @ w_in[A:2 * A].T
+    v = xn1 @ w_in[2 * A:3 * A].T
+    o, probs, lse = attention(dims, q, k, v)
+    hid = x + o @ w_out[:A]
+    xn2, xhat2, _, rstd2 = layernorm(hid, gamma2, beta2, dims["ln_eps"])
+    f = xn2 @ w_in[3 * A:].T
+    g = gelu(f)
+    y = hid + g @ w_out[A:]
+    saved = dict(xn1=xn1, xhat1=xhat1, rstd1=rstd1, q=q, k=k, v=v, o=o, probs=probs, lse=lse,
+                 h=hid, xn2=xn2, xhat2=xhat2, rstd2=rstd2, f=f, g=g)
+    return y, saved
+
+
+def serial_block_backward(dims, gamma1, gamma2, w_in, w_out, saved, dy):
+    """Gradients of sum(y * dy) through the serial block, sub-layer by
+    sub-layer in reverse: FC2, GeLU, FC1, LN2 (plus the residual into h),
+    the attention output projection, SWA, the Q/K/V projection, LN1 (plus
+    the residual into x)."""
+    b, s, H, d, A, _ = _split(dims)
+    w_in, w_out, dy = _f64(w_in), _f64(w_out), _f64(dy)
+    dw_fc2 = saved["g"].T @ dy
+    df = (dy @ w_out[A:].T) * gelu_grad(saved["f"])
+    dw_fc1 = df.T @ saved["xn2"]
+    dxn2 = df @ w_in[3 * A:]
+    dh_ln, dgamma2, dbeta2 = layernorm_backward(dxn2, saved["xhat2"], saved["rstd2"], gamma2)
+    dh = dy + dh_ln
+    dw_o = saved["o"].T @ dh
+    d_o = dh @ w_out[:A].T
+    dq = np.zeros_like(d_o)
+    dk = np.zeros_like(d_o)
+    dv = np.zeros_like(d_o)
+    for bi in range(b):
+        rows = slice(bi * s, (bi + 1) * s)
+        for hh in range(H):
+            cols = slice(hh * d, (hh + 1) * d)
+            dq[rows, cols], dk[rows, cols], dv[rows, cols] = swa_head_backward(
+                saved["q"][rows, cols], saved["k"][rows, cols], saved["v"][rows, cols],
+                saved["probs"][(bi, hh)], d_o[rows, cols])
+    dqkv = np.concatenate([dq, dk, dv], axis=1)
+    dw_qkv = dqkv.T @ saved["xn1"]
+    dxn1 = dqkv @ w_in[:3 * A]
+    dx_ln, dgamma1, dbeta1 = layernorm_backward(dxn1, saved["xhat1"], saved["rstd1"], gamma1)
+    return dict(dx=dh + dx_ln, dgamma1=dgamma1, dbeta1=dbeta1, dgamma2=dgamma2, dbeta2=dbeta2,
+                dw_in=np.concatenate([dw_qkv, dw_fc1], axis=0),
+                dw_out=np.concatenate([dw_o, dw_fc2], axis=0), dh=dh, d_o=d_o)
 
 
 def ptb_backward(dims, x, gamma, w_in, w_out, saved, dy):

@@ -44,3 +44,30 @@ def layer_with_grads(dims, inputs):
     dy = torch.tensor(inputs["dy"], dtype=torch.float64)
     (y * dy).sum().backward()
     return y.detach().numpy(), {k: leaves[k].grad.numpy() for k in names}
+
+
+def serial_layer(dims, x, gamma1, beta1, gamma2, beta2, w_in, w_out):
+    """The serial pre-LN block: h = x + Attention(LN1(x)); y = h + MLP(LN2(h))."""
+    b, s, H, d = dims["batch"], dims["seq"], dims["n_heads"], dims["head_dim"]
+    A = H * d
+    xn1 = F.layer_norm(x, (x.shape[1],), gamma1, beta1, dims["ln_eps"])
+
+    def heads(t):
+        return t.reshape(b, s, H, d).permute(0, 2, 1, 3)
+
+    o = F.scaled_dot_product_attention(heads(F.linear(xn1, w_in[:A])),
+                                       heads(F.linear(xn1, w_in[A:2 * A])),
+                                       heads(F.linear(xn1, w_in[2 * A:3 * A])),
+                                       attn_mask=band_mask(s, dims["window"]))
+    hid = x + o.permute(0, 2, 1, 3).reshape(b * s, A) @ w_out[:A]
+    xn2 = F.layer_norm(hid, (hid.shape[1],), gamma2, beta2, dims["ln_eps"])
+    return hid + F.gelu(F.linear(xn2, w_in[3 * A:])) @ w_out[A:]
+
+
+def serial_layer_with_grads(dims, inputs):
+    names = ("x", "gamma1", "beta1", "gamma2", "beta2", "w_in", "w_out")
+    leaves = {k: torch.tensor(inputs[k], dtype=torch.float64, requires_grad=True) for k in names}
+    y = serial_layer(dims, *(leaves[k] for k in names))
+    dy = torch.tensor(inputs["dy"], dtype=torch.float64)
+    (y * dy).sum().backward()
+    return y.detach().numpy(), {k: leaves[k].grad.numpy() for k in names}
