@@ -15,7 +15,9 @@ the MegaScale study guide, ch.2 §2.1) over the measured fwd+bwd time; `mfu`
 divides it by the bf16 dense MFMA peak; `lamb_gbps` is the LAMB step's
 algorithmic bytes over its time.  `roofline` describes the dominant kernel
 stage; `cpu_baseline` times the fp64 CPU oracle on one full step's forward and
-backward of the same workload.
+backward of the same workload; `serial` times the serial pre-LN block (two
+LayerNorms, four separate projections) on the same workload and weights, the
+arrangement the PTB replaces.
 
     python bench.py [--steps K] [--warmup W] [--config 175b_w512]
 """
@@ -41,6 +43,8 @@ def parse():
     p.add_argument("--config", default="175b_w512")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the fp64 CPU oracle")
+    p.add_argument("--no-serial", action="store_true",
+                   help="skip timing the serial pre-LN block on the same workload")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run one plain device-to-device copy of MIB MiB and exit (the "
@@ -90,6 +94,34 @@ def lamb_bytes(params):
         total += n * (4 + g + 4 + 4 + 4 + 4)            # pass A
         total += n * (12 + 4 + (2 if p.get("w_bf16") is not None else 0))  # pass B
     return total
+
+
+def time_serial(cfg, inputs, args, ptb_ms):
+    """Forward and backward of the serial pre-LN block on the same inputs and
+    weights (LN2 with unit gamma, zero beta), timed like the PTB step."""
+    import numpy as np
+    import torch
+    from transformer_block_lamb_amd.device import SerialShard
+    from transformer_block_lamb_amd.synth import second_ln_params
+    g2, b2 = second_ln_params(cfg)
+    ser = SerialShard(cfg, inputs, g2, b2)
+    for _ in range(args.warmup):
+        ser.forward()
+        ser.backward()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record()
+        ser.forward()
+        ev[k][1].record()
+        ser.backward()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    del ser
+    return {"fwd_ms": round(f, 4), "bwd_ms": round(b, 4),
+            "ptb_speedup": round((f + b) / ptb_ms, 4)}
 
 
 def cpu_baseline(cfg, inputs, model_flops):
@@ -206,6 +238,10 @@ def main():
     bwd_ms = sum(v for n, v in per_stage.items() if n.startswith("bwd."))
     lamb_ms = per_stage["lamb"]
 
+    serial = None
+    if not args.no_serial:
+        serial = time_serial(cfg, inputs, args, fwd_ms + bwd_ms)
+
     flops = stage_flops(cfg)
     n_mat = (3 * A + F) * cfg.hidden + (A + F) * cfg.hidden
     model_flops = 6.0 * n_mat * cfg.tokens
@@ -239,6 +275,10 @@ def main():
         "stages_ms": {n: round(v, 4) for n, v in per_stage.items()},
         "roofline": roofline,
     }
+    if serial is not None:
+        serial["model_tflops"] = round(model_flops / ((serial["fwd_ms"] + serial["bwd_ms"]) * 1e-3)
+                                       / 1e12, 2)
+        out["serial"] = serial
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inputs, model_flops)
     line = json.dumps(out)

@@ -106,6 +106,32 @@ int ptb_backward(const ptb_dims* dims, const void* x, const float* ln_gamma,
                  float* d_ln_beta, void* dw_in, void* dw_out, void* scratch,
                  size_t scratch_bytes, hipStream_t stream);
 
+/* The serial pre-LN block that the PTB row replaces (same study guide page,
+ * ch.2 §2.2 technique table, PTB row, which writes the serial form with the
+ * attention residual missing; read here as the standard pre-LN layer):
+ *   h = x + Attention(LN1(x));   y = h + MLP(LN2(h)).
+ * Same dims, kernels and weight layout as ptb_forward (w_in rows
+ * Q | K | V | FC1, w_out rows attention-out | FC2), but two LayerNorms with
+ * their own fp32 (gamma, beta) and four separate projections.  LN2 needs the
+ * whole h, so dims->add_residual must be 1 (else PTB_ERR_INVALID_ARG); on a
+ * tensor-parallel shard this computes the shard's weights as a whole layer.
+ * Buffers and errors as for ptb_forward / ptb_backward; sizes from
+ * ptb_serial_saved_bytes / ptb_serial_scratch_bytes (bf16: each includes a
+ * 128 MiB GEMM workspace tail).  Backward overwrites dx, the four LN
+ * gradients (fp32), dw_in and dw_out. */
+size_t ptb_serial_saved_bytes(const ptb_dims* dims);
+size_t ptb_serial_scratch_bytes(const ptb_dims* dims);
+int ptb_serial_forward(const ptb_dims* dims, const void* x, const float* ln1_gamma,
+                       const float* ln1_beta, const float* ln2_gamma, const float* ln2_beta,
+                       const void* w_in, const void* w_out, void* y, void* saved,
+                       size_t saved_bytes, hipStream_t stream);
+int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_gamma,
+                        const float* ln2_gamma, const void* w_in, const void* w_out,
+                        const void* saved, size_t saved_bytes, const void* dy, void* dx,
+                        float* d_ln1_gamma, float* d_ln1_beta, float* d_ln2_gamma,
+                        float* d_ln2_beta, void* dw_in, void* dw_out, void* scratch,
+                        size_t scratch_bytes, hipStream_t stream);
+
 /* One parameter tensor for lamb_step.
  *   w, m, v    fp32 device arrays of n elements, updated in place
  *   g          gradient, n elements of grad_dtype (PTB_F32 or PTB_BF16)

@@ -107,3 +107,19 @@ def test_component_argument_checks():
     assert L.ptb_gemm(1, 0, 0, 16, 16, 16, fake, 16, fake, 16, fake, 16, 0, fake + 16, ws, None) == -3
     assert L.ptb_layernorm_forward(1, 4, 12, fake, fake, fake, 1e-5, fake, fake, fake, None) == -1
     assert B.ptb_status_string(-3).startswith("workspace")
+
+
+def test_serial_block_sizes_and_checks():
+    d = dims()
+    assert B.ptb_serial_saved_bytes(d) > B.ptb_saved_bytes(d)  # h and LN2's output kept too
+    assert B.ptb_serial_scratch_bytes(d) > 0
+    # LN2 needs the whole h: the serial block always carries both residuals
+    d0 = dims(add_residual=0)
+    assert B.ptb_serial_saved_bytes(d0) == 0
+    L = B.lib()
+    fake = 0x10000
+    args = [fake] * 7
+    assert L.ptb_serial_forward(ctypes.byref(d0), *args, fake, fake, 1 << 40, None) == -1
+    need = B.ptb_serial_saved_bytes(d)
+    assert L.ptb_serial_forward(ctypes.byref(d), *args, fake, fake, need - 1, None) == -3
+    assert L.ptb_serial_forward(ctypes.byref(d), fake + 4, *args[1:], fake, fake, need, None) == -1

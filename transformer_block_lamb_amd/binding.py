@@ -22,7 +22,8 @@ EXPORTED = ("ptb_saved_bytes", "ptb_scratch_bytes", "ptb_forward", "ptb_backward
             "lamb_scratch_bytes", "lamb_step", "ptb_status_string",
             "ptb_forward_stage", "ptb_backward_stage",
             "ptb_layernorm_forward", "ptb_gemm_workspace_bytes", "ptb_gemm", "ptb_swa_forward",
-            "ptb_swa_backward")
+            "ptb_swa_backward", "ptb_serial_saved_bytes", "ptb_serial_scratch_bytes",
+            "ptb_serial_forward", "ptb_serial_backward")
 FWD_STAGES = ("layernorm", "gemm_in", "attention", "gemm_out")
 BWD_STAGES = ("gemm_dcat", "gemm_dw_out", "attention", "gemm_dw_in", "gemm_dxn", "layernorm")
 
@@ -80,6 +81,11 @@ def lib():
                                         i32, vp, ctypes.c_size_t, vp]),
             "ptb_swa_forward": (ctypes.c_int, [pd, vp, vp, i64, vp, vp]),
             "ptb_swa_backward": (ctypes.c_int, [pd, vp, vp, i64, vp, vp, vp, vp, vp]),
+            "ptb_serial_saved_bytes": (sz, [pd]),
+            "ptb_serial_scratch_bytes": (sz, [pd]),
+            "ptb_serial_forward": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ptb_serial_backward": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp,
+                                                   vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -226,3 +232,29 @@ def ptb_swa_backward(dims, qkv, o, ldo, d_o, lse, dqkv, dvec, stream=None):
     _check(lib().ptb_swa_backward(ctypes.byref(dims), _ptr(qkv), _ptr(o), ldo, _ptr(d_o),
                                   _ptr(lse), _ptr(dqkv), _ptr(dvec), _stream(stream)),
            "ptb_swa_backward")
+
+
+def ptb_serial_saved_bytes(dims: PtbDims) -> int:
+    return int(lib().ptb_serial_saved_bytes(ctypes.byref(dims)))
+
+
+def ptb_serial_scratch_bytes(dims: PtbDims) -> int:
+    return int(lib().ptb_serial_scratch_bytes(ctypes.byref(dims)))
+
+
+def ptb_serial_forward(dims, x, ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, w_in, w_out, y, saved,
+                       stream=None):
+    _check(lib().ptb_serial_forward(ctypes.byref(dims), _ptr(x), _ptr(ln1_gamma), _ptr(ln1_beta),
+                                    _ptr(ln2_gamma), _ptr(ln2_beta), _ptr(w_in), _ptr(w_out),
+                                    _ptr(y), _ptr(saved), _nbytes(saved), _stream(stream)),
+           "ptb_serial_forward")
+
+
+def ptb_serial_backward(dims, x, ln1_gamma, ln2_gamma, w_in, w_out, saved, dy, dx, d_ln1_gamma,
+                        d_ln1_beta, d_ln2_gamma, d_ln2_beta, dw_in, dw_out, scratch, stream=None):
+    _check(lib().ptb_serial_backward(ctypes.byref(dims), _ptr(x), _ptr(ln1_gamma), _ptr(ln2_gamma),
+                                     _ptr(w_in), _ptr(w_out), _ptr(saved), _nbytes(saved), _ptr(dy),
+                                     _ptr(dx), _ptr(d_ln1_gamma), _ptr(d_ln1_beta),
+                                     _ptr(d_ln2_gamma), _ptr(d_ln2_beta), _ptr(dw_in), _ptr(dw_out),
+                                     _ptr(scratch), _nbytes(scratch), _stream(stream)),
+           "ptb_serial_backward")

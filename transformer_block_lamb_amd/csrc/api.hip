@@ -171,7 +171,8 @@ int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const 
         g.n_split = (int)(2 * d.A);
         g.ws = ws;
         g.ws_bytes = ws_bytes;
-        e = launch_gemm_in_fwd(dt, g, qkv, qk_lo, f, cat, (int)d.A, (int)d.F, stream);
+        e = launch_gemm_in_fwd(dt, g, qkv, qk_lo, f, cat, (int)d.A, (int)d.F, (int)(3 * d.A),
+                               stream);
         break;
       }
       case PTB_FWD_ATTENTION:
@@ -237,7 +238,7 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
         GemmDesc g{(int)d.T, (int)d.K2, (int)d.h, kKContig, kKContig, dy, d.h, w_out, d.h};
         g.ws = ws;
         g.ws_bytes = ws_bytes;
-        e = launch_gemm_dcat(dt, g, f, d_o, dz, (int)d.A, (int)d.F, stream);
+        e = launch_gemm_dcat(dt, g, f, d_o, dz, (int)d.A, (int)d.F, d.N1, 3 * d.A, stream);
         break;
       }
       case PTB_BWD_GEMM_DW_OUT: {  // dw_out = cat^T dy
@@ -285,6 +286,231 @@ int ptb_backward(const ptb_dims* dims, const void* x, const float* ln_gamma, con
                  void* scratch, size_t scratch_bytes, hipStream_t stream) {
   return ptb_backward_stage(dims, -1, x, ln_gamma, w_in, w_out, saved, saved_bytes, dy, dx,
                             d_ln_gamma, d_ln_beta, dw_in, dw_out, scratch, scratch_bytes, stream);
+}
+
+// ------------------------------------------------------------------ serial block
+// h = x + Attention(LN1(x)); y = h + MLP(LN2(h)) on the same kernels and the
+// same w_in / w_out layout as the PTB, with unfused projections.
+namespace {
+
+struct SerialSavedLayout {
+  size_t xn1, xn1_lo, qk_lo, qkv, cat, hid, xn2, f, mean1, rstd1, mean2, rstd2, lse, gemm_ws,
+      total;
+  explicit SerialSavedLayout(const Dims& d) {
+    const bool split = d.e == 2;
+    size_t o = 0;
+    xn1 = o;    o += up(d.T * d.h * d.e);
+    xn1_lo = o; o += split ? up(d.T * d.h * 2) : 0;
+    qk_lo = o;  o += split ? up(d.T * 2 * d.A * 2) : 0;
+    qkv = o;    o += up(d.T * 3 * d.A * d.e);
+    cat = o;    o += up(d.T * d.K2 * d.e);
+    hid = o;    o += up(d.T * d.h * d.e);
+    xn2 = o;    o += up(d.T * d.h * d.e);
+    f = o;      o += up(d.T * d.F * d.e);
+    mean1 = o;  o += up(d.T * 4);
+    rstd1 = o;  o += up(d.T * 4);
+    mean2 = o;  o += up(d.T * 4);
+    rstd2 = o;  o += up(d.T * 4);
+    lse = o;    o += up(d.B * d.H * d.S * 4);
+    gemm_ws = o; o += split ? kGemmWsBytes : 0;
+    total = o;
+  }
+};
+
+struct SerialScratchLayout {
+  size_t d_o, dz, dxn, dh, dvec, gpart, bpart, gemm_ws, total;
+  explicit SerialScratchLayout(const Dims& d) {
+    const int64_t nblk = (d.T + ln_bwd_rows_per_block() - 1) / ln_bwd_rows_per_block();
+    size_t o = 0;
+    d_o = o;   o += up(d.T * d.A * d.e);
+    dz = o;    o += up(d.T * d.N1 * d.e);
+    dxn = o;   o += up(d.T * d.h * 4);
+    dh = o;    o += up(d.T * d.h * d.e);
+    dvec = o;  o += up(d.B * d.H * d.S * 4);
+    gpart = o; o += up(nblk * d.h * 4);
+    bpart = o; o += up(nblk * d.h * 4);
+    gemm_ws = o; o += d.e == 2 ? kGemmWsBytes : 0;
+    total = o;
+  }
+};
+
+int check_serial_dims(const ptb_dims* d) {
+  const int st = check_dims(d);
+  if (st != PTB_OK) return st;
+  // LN2 normalises the whole h, so the serial block has both residuals
+  return d->add_residual == 1 ? PTB_OK : PTB_ERR_INVALID_ARG;
+}
+
+const char* off(const void* p, int64_t elems, size_t e) {
+  return static_cast<const char*>(p) + elems * (int64_t)e;
+}
+
+}  // namespace
+
+size_t ptb_serial_saved_bytes(const ptb_dims* d) {
+  if (check_serial_dims(d) != PTB_OK) return 0;
+  return SerialSavedLayout(Dims(d)).total;
+}
+
+size_t ptb_serial_scratch_bytes(const ptb_dims* d) {
+  if (check_serial_dims(d) != PTB_OK) return 0;
+  return SerialScratchLayout(Dims(d)).total;
+}
+
+int ptb_serial_forward(const ptb_dims* dims, const void* x, const float* ln1_gamma,
+                       const float* ln1_beta, const float* ln2_gamma, const float* ln2_beta,
+                       const void* w_in, const void* w_out, void* y, void* saved,
+                       size_t saved_bytes, hipStream_t stream) {
+  int st = check_serial_dims(dims);
+  if (st != PTB_OK) return st;
+  if (!all_aligned({x, ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, w_in, w_out, y, saved}))
+    return PTB_ERR_INVALID_ARG;
+  const Dims d(dims);
+  const SerialSavedLayout L(d);
+  if (saved_bytes < L.total) return PTB_ERR_WORKSPACE;
+  const int dt = dims->dtype;
+  const bool bf = dt == PTB_BF16;
+  void* xn1 = at<char>(saved, L.xn1);
+  void* xn1_lo = bf ? at<char>(saved, L.xn1_lo) : nullptr;
+  void* qk_lo = bf ? at<char>(saved, L.qk_lo) : nullptr;
+  void* qkv = at<char>(saved, L.qkv);
+  void* cat = at<char>(saved, L.cat);
+  void* hid = at<char>(saved, L.hid);
+  void* xn2 = at<char>(saved, L.xn2);
+  void* f = at<char>(saved, L.f);
+  void* ws = bf ? at<char>(saved, L.gemm_ws) : nullptr;
+  const size_t wsb = bf ? kGemmWsBytes : 0;
+  const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
+                   3 * d.A, qk_lo};
+  hipError_t e = launch_ln_fwd(dt, x, ln1_gamma, ln1_beta, dims->ln_eps, (int)d.T, (int)d.h, xn1,
+                               xn1_lo, at<float>(saved, L.mean1), at<float>(saved, L.rstd1),
+                               stream);
+  if (e == hipSuccess) {  // [q|k|v] = xn1 w_qkv^T (q, k with the second pass over xn1_lo)
+    GemmDesc g{(int)d.T, (int)(3 * d.A), (int)d.h, kKContig, kKContig, xn1, d.h, w_in, d.h};
+    g.a2 = xn1_lo;
+    g.n_split = (int)(2 * d.A);
+    g.ws = ws;
+    g.ws_bytes = wsb;
+    e = launch_gemm_in_fwd(dt, g, qkv, qk_lo, f, cat, (int)d.A, (int)d.F, (int)(3 * d.A), stream);
+  }
+  if (e == hipSuccess) e = launch_swa_fwd(dt, sw, cat, d.K2, at<float>(saved, L.lse), stream);
+  if (e == hipSuccess) {  // h = x + O w_o
+    GemmDesc g{(int)d.T, (int)d.h, (int)d.A, kKContig, kMNContig, cat, d.K2, w_out, d.h};
+    g.ws = ws;
+    g.ws_bytes = wsb;
+    e = launch_gemm_out_fwd(dt, g, x, 1, hid, stream);
+  }
+  if (e == hipSuccess)
+    e = launch_ln_fwd(dt, hid, ln2_gamma, ln2_beta, dims->ln_eps, (int)d.T, (int)d.h, xn2,
+                      nullptr, at<float>(saved, L.mean2), at<float>(saved, L.rstd2), stream);
+  if (e == hipSuccess) {  // f = xn2 w_fc1^T, GeLU(f) into cat[:, A:]
+    GemmDesc g{(int)d.T, (int)d.F, (int)d.h, kKContig, kKContig, xn2, d.h,
+               off(w_in, 3 * d.A * d.h, d.e), d.h};
+    g.ws = ws;
+    g.ws_bytes = wsb;
+    e = launch_gemm_in_fwd(dt, g, qkv, nullptr, f, cat, (int)d.A, (int)d.F, 0, stream);
+  }
+  if (e == hipSuccess) {  // y = h + GeLU(f) w_fc2
+    GemmDesc g{(int)d.T, (int)d.h, (int)d.F, kKContig, kMNContig, off(cat, d.A, d.e), d.K2,
+               off(w_out, d.A * d.h, d.e), d.h};
+    g.ws = ws;
+    g.ws_bytes = wsb;
+    e = launch_gemm_out_fwd(dt, g, hid, 1, y, stream);
+  }
+  return e == hipSuccess ? PTB_OK : PTB_ERR_HIP;
+}
+
+int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_gamma,
+                        const float* ln2_gamma, const void* w_in, const void* w_out,
+                        const void* saved, size_t saved_bytes, const void* dy, void* dx,
+                        float* d_ln1_gamma, float* d_ln1_beta, float* d_ln2_gamma,
+                        float* d_ln2_beta, void* dw_in, void* dw_out, void* scratch,
+                        size_t scratch_bytes, hipStream_t stream) {
+  int st = check_serial_dims(dims);
+  if (st != PTB_OK) return st;
+  if (!all_aligned({x, ln1_gamma, ln2_gamma, w_in, w_out, saved, dy, dx, d_ln1_gamma, d_ln1_beta,
+                    d_ln2_gamma, d_ln2_beta, dw_in, dw_out, scratch}))
+    return PTB_ERR_INVALID_ARG;
+  const Dims d(dims);
+  const SerialSavedLayout L(d);
+  const SerialScratchLayout R(d);
+  if (saved_bytes < L.total || scratch_bytes < R.total) return PTB_ERR_WORKSPACE;
+  const int dt = dims->dtype;
+  const bool bf = dt == PTB_BF16;
+  const void* xn1 = at<char>(saved, L.xn1);
+  const void* qk_lo = bf ? at<char>(saved, L.qk_lo) : nullptr;
+  const void* qkv = at<char>(saved, L.qkv);
+  const void* cat = at<char>(saved, L.cat);
+  const void* hid = at<char>(saved, L.hid);
+  const void* xn2 = at<char>(saved, L.xn2);
+  const void* f = at<char>(saved, L.f);
+  void* d_o = at<char>(scratch, R.d_o);
+  void* dz = at<char>(scratch, R.dz);
+  float* dxn = at<float>(scratch, R.dxn);
+  void* dh = at<char>(scratch, R.dh);
+  float* gpart = at<float>(scratch, R.gpart);
+  float* bpart = at<float>(scratch, R.bpart);
+  void* ws = bf ? at<char>(scratch, R.gemm_ws) : nullptr;
+  const size_t wsb = bf ? kGemmWsBytes : 0;
+  const int nblk = (int)((d.T + ln_bwd_rows_per_block() - 1) / ln_bwd_rows_per_block());
+  const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
+                   3 * d.A, qk_lo};
+  auto gemm = [&](int M, int N, int K, int al, int bl, const void* a, int64_t lda, const void* b,
+                  int64_t ldb) {
+    GemmDesc g{M, N, K, al, bl, a, lda, b, ldb};
+    g.ws = ws;
+    g.ws_bytes = wsb;
+    return g;
+  };
+  char* dw_in_c = static_cast<char*>(dw_in);
+  char* dw_out_c = static_cast<char*>(dw_out);
+  // MLP sub-layer: dw_fc2 = GeLU(f)^T dy; df = (dy w_fc2^T) GeLU'(f) into dz[:, 3A:]
+  hipError_t e = launch_gemm_store(
+      dt, gemm((int)d.F, (int)d.h, (int)d.T, kMNContig, kMNContig, off(cat, d.A, d.e), d.K2, dy, d.h),
+      dw_out_c + d.A * d.h * d.e, d.h, false, stream);
+  if (e == hipSuccess)
+    e = launch_gemm_dcat(dt, gemm((int)d.T, (int)d.F, (int)d.h, kKContig, kKContig, dy, d.h,
+                                  off(w_out, d.A * d.h, d.e), d.h),
+                         f, d_o, dz, 0, (int)d.F, d.N1, 3 * d.A, stream);
+  if (e == hipSuccess)  // dw_fc1 = df^T xn2
+    e = launch_gemm_store(dt, gemm((int)d.F, (int)d.h, (int)d.T, kMNContig, kMNContig,
+                                   off(dz, 3 * d.A, d.e), d.N1, xn2, d.h),
+                          dw_in_c + 3 * d.A * d.h * d.e, d.h, false, stream);
+  if (e == hipSuccess)  // dxn2 = df w_fc1 (fp32)
+    e = launch_gemm_store(dt, gemm((int)d.T, (int)d.h, (int)d.F, kKContig, kMNContig,
+                                   off(dz, 3 * d.A, d.e), d.N1, off(w_in, 3 * d.A * d.h, d.e), d.h),
+                          dxn, d.h, true, stream);
+  if (e == hipSuccess)  // dh = dy + LN2 backward
+    e = launch_ln_bwd(dt, hid, ln2_gamma, at<float>(saved, L.mean2), at<float>(saved, L.rstd2),
+                      dxn, dy, dh, gpart, bpart, (int)d.T, (int)d.h, stream);
+  if (e == hipSuccess)
+    e = launch_ln_bwd_reduce(gpart, bpart, nblk, (int)d.h, d_ln2_gamma, d_ln2_beta, stream);
+  // attention sub-layer: dw_o = O^T dh; dO = dh w_o^T
+  if (e == hipSuccess)
+    e = launch_gemm_store(dt, gemm((int)d.A, (int)d.h, (int)d.T, kMNContig, kMNContig, cat, d.K2,
+                                   dh, d.h),
+                          dw_out, d.h, false, stream);
+  if (e == hipSuccess)
+    e = launch_gemm_dcat(dt, gemm((int)d.T, (int)d.A, (int)d.h, kKContig, kKContig, dh, d.h, w_out,
+                                  d.h),
+                         f, d_o, dz, (int)d.A, (int)d.F, d.N1, 3 * d.A, stream);
+  if (e == hipSuccess)  // -> dz[:, :3A]
+    e = launch_swa_bwd(dt, sw, cat, d.K2, d_o, d.A, at<float>(saved, L.lse),
+                       at<float>(scratch, R.dvec), dz, d.N1, stream);
+  if (e == hipSuccess)  // dw_qkv = dqkv^T xn1
+    e = launch_gemm_store(dt, gemm((int)(3 * d.A), (int)d.h, (int)d.T, kMNContig, kMNContig, dz,
+                                   d.N1, xn1, d.h),
+                          dw_in, d.h, false, stream);
+  if (e == hipSuccess)  // dxn1 = dqkv w_qkv (fp32)
+    e = launch_gemm_store(dt, gemm((int)d.T, (int)d.h, (int)(3 * d.A), kKContig, kMNContig, dz,
+                                   d.N1, w_in, d.h),
+                          dxn, d.h, true, stream);
+  if (e == hipSuccess)  // dx = dh + LN1 backward
+    e = launch_ln_bwd(dt, x, ln1_gamma, at<float>(saved, L.mean1), at<float>(saved, L.rstd1), dxn,
+                      dh, dx, gpart, bpart, (int)d.T, (int)d.h, stream);
+  if (e == hipSuccess)
+    e = launch_ln_bwd_reduce(gpart, bpart, nblk, (int)d.h, d_ln1_gamma, d_ln1_beta, stream);
+  return e == hipSuccess ? PTB_OK : PTB_ERR_HIP;
 }
 
 size_t lamb_scratch_bytes(const lamb_tensor* t, int32_t n) {

@@ -139,19 +139,22 @@ struct EpiOutFwd {
   }
 };
 
+// Columns < attn go to d_o [T, attn]; column attn + c (c < ffn) goes, times
+// GeLU'(f[:, c]), to dz[row * dz_ld + dz_off + c].
 template <typename T>
 struct EpiDcat {
   const T* f;
   T* d_o;
   T* dz;
   int attn, ffn;
+  int64_t dz_ld, dz_off;
   __device__ __forceinline__ void operator()(int row, int col, float v) const {
     if (col < attn) {
       Elt<T>::st(d_o + (int64_t)row * attn + col, v);
     } else {
       const int c = col - attn;
       const float fv = Elt<T>::ld(f + (int64_t)row * ffn + c);
-      Elt<T>::st(dz + (int64_t)row * (3 * attn + ffn) + 3 * attn + c, v * gelu_grad_f(fv));
+      Elt<T>::st(dz + row * dz_ld + dz_off + c, v * gelu_grad_f(fv));
     }
   }
   // attn is a multiple of 8, so a chunk never straddles the O / FC2 border
@@ -165,7 +168,7 @@ struct EpiDcat {
       get8(f + (int64_t)row * ffn + c, fv, valid);
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = v[e] * gelu_grad_f(fv[e]);
-      put8(dz + (int64_t)row * (3 * attn + ffn) + 3 * attn + c, r, valid);
+      put8(dz + row * dz_ld + dz_off + c, r, valid);
     }
   }
 };
@@ -856,13 +859,13 @@ hipError_t launch_gemm_store(int dtype, const GemmDesc& d, void* c, int64_t ldc,
 }
 
 hipError_t launch_gemm_in_fwd(int dtype, const GemmDesc& d, void* qkv, void* qk_lo, void* f,
-                              void* cat, int attn, int ffn, hipStream_t s) {
+                              void* cat, int attn, int ffn, int qkv_cols, hipStream_t s) {
   if (dtype == 1) {
-    EpiInFwd<bf16_t> e{(bf16_t*)qkv, (bf16_t*)qk_lo, (bf16_t*)f, (bf16_t*)cat, 3 * attn, attn,
+    EpiInFwd<bf16_t> e{(bf16_t*)qkv, (bf16_t*)qk_lo, (bf16_t*)f, (bf16_t*)cat, qkv_cols, attn,
                        ffn};
     return run_layouts<EpiInFwd<bf16_t>, true>(d, e, s);
   }
-  EpiInFwd<float> e{(float*)qkv, nullptr, (float*)f, (float*)cat, 3 * attn, attn, ffn};
+  EpiInFwd<float> e{(float*)qkv, nullptr, (float*)f, (float*)cat, qkv_cols, attn, ffn};
   return run_layouts<EpiInFwd<float>, false>(d, e, s);
 }
 
@@ -877,12 +880,12 @@ hipError_t launch_gemm_out_fwd(int dtype, const GemmDesc& d, const void* x, int 
 }
 
 hipError_t launch_gemm_dcat(int dtype, const GemmDesc& d, const void* f, void* d_o, void* dz,
-                            int attn, int ffn, hipStream_t s) {
+                            int attn, int ffn, int64_t dz_ld, int64_t dz_off, hipStream_t s) {
   if (dtype == 1) {
-    EpiDcat<bf16_t> e{(const bf16_t*)f, (bf16_t*)d_o, (bf16_t*)dz, attn, ffn};
+    EpiDcat<bf16_t> e{(const bf16_t*)f, (bf16_t*)d_o, (bf16_t*)dz, attn, ffn, dz_ld, dz_off};
     return run_layouts<EpiDcat<bf16_t>, true>(d, e, s);
   }
-  EpiDcat<float> e{(const float*)f, (float*)d_o, (float*)dz, attn, ffn};
+  EpiDcat<float> e{(const float*)f, (float*)d_o, (float*)dz, attn, ffn, dz_ld, dz_off};
   return run_layouts<EpiDcat<float>, false>(d, e, s);
 }
 

@@ -48,19 +48,20 @@ hipError_t launch_ln_bwd_reduce(const float* gpart, const float* bpart, int nblk
 // Plain product stored in the operand dtype (or fp32 when c_f32).
 hipError_t launch_gemm_store(int dtype, const GemmDesc& g, void* c, int64_t ldc, bool c_f32,
                              hipStream_t s);
-// Input projection of the block: columns < 3A go to qkv [T, 3A] (and, for
-// the q and k columns, their bf16 rounding residual to qk_lo [T, 2A] when
-// qk_lo is not null); the FC1 columns go to f [T, F] (pre-activation) and
-// GeLU(f) to cat[:, A:].
+// Input projection of the block: columns < qkv_cols (3A for the fused
+// projection, 0 for FC1 alone) go to qkv [T, qkv_cols] (and, for the q and
+// k columns, their bf16 rounding residual to qk_lo [T, 2A] when qk_lo is not
+// null); the FC1 columns go to f [T, F] (pre-activation) and GeLU(f) to
+// cat[:, A:].
 hipError_t launch_gemm_in_fwd(int dtype, const GemmDesc& g, void* qkv, void* qk_lo, void* f,
-                              void* cat, int attn_width, int ffn, hipStream_t s);
+                              void* cat, int attn_width, int ffn, int qkv_cols, hipStream_t s);
 // Output projection plus optional residual: y = acc (+ x).
 hipError_t launch_gemm_out_fwd(int dtype, const GemmDesc& g, const void* x, int add_residual,
                                void* y, hipStream_t s);
 // Backward of the output projection w.r.t. cat (dcat = dy w_out^T): columns < A go to dO [T, A];
-// the FC2 columns are multiplied by GeLU'(f) and go to dz[:, 3A:].
+// FC2 column c is multiplied by GeLU'(f[:, c]) and goes to dz[t * dz_ld + dz_off + c].
 hipError_t launch_gemm_dcat(int dtype, const GemmDesc& g, const void* f, void* d_o, void* dz,
-                            int attn_width, int ffn, hipStream_t s);
+                            int attn_width, int ffn, int64_t dz_ld, int64_t dz_off, hipStream_t s);
 
 // ---- swa.hip
 struct SwaDesc {

@@ -65,6 +65,42 @@ class PtbShard:
                     dw_in=f(self.dw_in), dw_out=f(self.dw_out))
 
 
+class SerialShard(PtbShard):
+    """The serial pre-LN block on the same inputs and weights as a PtbShard,
+    plus the second LayerNorm's (gamma2, beta2)."""
+
+    def __init__(self, cfg, inputs: dict, gamma2, beta2, device="cuda"):
+        super().__init__(cfg, inputs, device)
+        self.gamma2 = to_device(gamma2, torch.float32, device)
+        self.beta2 = to_device(beta2, torch.float32, device)
+        self.dgamma2 = torch.empty_like(self.gamma2)
+        self.dbeta2 = torch.empty_like(self.beta2)
+        self.saved = torch.empty(B.ptb_serial_saved_bytes(self.dims), dtype=torch.uint8,
+                                 device=device)
+        self.scratch = torch.empty(B.ptb_serial_scratch_bytes(self.dims), dtype=torch.uint8,
+                                   device=device)
+
+    def forward(self, stream=None):
+        B.ptb_serial_forward(self.dims, self.x, self.gamma, self.beta, self.gamma2, self.beta2,
+                             self.w_in, self.w_out, self.y, self.saved, stream)
+
+    def backward(self, stream=None):
+        B.ptb_serial_backward(self.dims, self.x, self.gamma, self.gamma2, self.w_in, self.w_out,
+                              self.saved, self.dy, self.dx, self.dgamma, self.dbeta, self.dgamma2,
+                              self.dbeta2, self.dw_in, self.dw_out, self.scratch, stream)
+
+    def forward_stage(self, stage, stream=None):
+        raise NotImplementedError("the serial block runs as whole forward / backward calls")
+
+    backward_stage = forward_stage
+
+    def outputs(self) -> dict:
+        out = super().outputs()
+        f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+        out.update(dgamma2=f(self.dgamma2), dbeta2=f(self.dbeta2))
+        return out
+
+
 class LambState:
     """Device copies of per-tensor (w, g, m, v) plus the scratch of one step.
 

@@ -138,6 +138,15 @@ def ptb_inputs(cfg: PtbConfig, seed: int = SEED, ln_affine: str = "unit",
     return out
 
 
+def second_ln_params(cfg: PtbConfig, seed: int = SEED + 2, ln_affine: str = "unit"):
+    """(gamma2, beta2) fp32 for the serial block's second LayerNorm."""
+    h = cfg.hidden
+    if ln_affine == "unit":
+        return np.ones(h, np.float32), np.zeros(h, np.float32)
+    r = _streams(seed, 2)
+    return _normal(r[0], (h,), 0.1, 1.0), _normal(r[1], (h,), 0.1)
+
+
 def lamb_inputs(sizes, seed: int = SEED + 1, grad_std: float = 1e-3,
                 grad_dtype: str = "bf16", gamma_beta_tail: bool = True) -> list:
     """Per tensor: fp32 master w, bf16-exact (or fp32) gradient g, m = v = 0.
