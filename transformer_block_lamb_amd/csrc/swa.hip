@@ -53,38 +53,66 @@ __device__ __forceinline__ bf16x8_t pack8(const float* v) {
 }
 __device__ __forceinline__ bool visible(int i, int j, int w) { return j <= i && i - j < w; }
 
-// Copy rows [r0, r0 + 64) x D of a token-major matrix into LDS row-major
-// (stride D + 8); rows at or beyond `seq` read as zero.
+// Register-staged copies of one 64-row tile, so the loads of the next tile
+// can be issued before the current one is consumed: load() issues every
+// global load of this thread's share at once, store() writes it to LDS.
+// RowTile: rows [r0, r0 + 64) x D into LDS row-major (stride D + 8); thread
+// t owns 16-byte chunks t, t + 256, ... (D / 32 of them).
 template <int D>
-__device__ __forceinline__ void stage_rows(bf16_t* dst, const bf16_t* src, int64_t ld, int r0,
-                                           int seq) {
-  constexpr int CH = D / 8;
-  for (int c = threadIdx.x; c < kBKV * CH; c += kSwaThreads) {
-    const int r = c / CH, cc = c - r * CH;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + r < seq) v = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * ld + cc * 8);
-    *reinterpret_cast<uint4*>(dst + r * (D + 8) + cc * 8) = v;
-  }
-}
-// Same rows stored transposed: dst[dim][row] with stride kTLD.
-template <int D>
-__device__ __forceinline__ void stage_rows_t(bf16_t* dst, const bf16_t* src, int64_t ld, int r0,
-                                             int seq) {
-  constexpr int NB = (kBKV / 8) * (D / 8);
-  for (int c = threadIdx.x; c < NB; c += kSwaThreads) {
-    const int rb = c & 7, db = c >> 3;
-    uint4 in[8], out[8];
+struct RowTile {
+  static constexpr int CH = D / 8, N = kBKV * CH / kSwaThreads;
+  static_assert(N * kSwaThreads == kBKV * CH, "whole chunks per thread");
+  uint4 v[N];
+  __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int r0, int seq) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = r0 + rb * 8 + i;
-      in[i] = r < seq ? *reinterpret_cast<const uint4*>(src + (int64_t)r * ld + db * 8)
-                      : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < N; ++i) {
+      const int c = threadIdx.x + i * kSwaThreads, r = c / CH, cc = c - r * CH;
+      v[i] = r0 + r < seq ? *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * ld + cc * 8)
+                          : make_uint4(0, 0, 0, 0);
     }
-    transpose8x8(in, out);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd)
-      *reinterpret_cast<uint4*>(dst + (db * 8 + dd) * kTLD + rb * 8) = out[dd];
   }
+  __device__ __forceinline__ void store(bf16_t* dst) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = threadIdx.x + i * kSwaThreads, r = c / CH, cc = c - r * CH;
+      *reinterpret_cast<uint4*>(dst + r * (D + 8) + cc * 8) = v[i];
+    }
+  }
+};
+// RowTileT: the same rows stored transposed, dst[dim][row] with stride kTLD;
+// thread t < D owns the 8-row x 8-dim block (rows 8 (t & 7), dims 8 (t >> 3))
+// and transposes it in registers.
+template <int D>
+struct RowTileT {
+  uint4 v[8];
+  __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int r0, int seq) {
+    const int t = threadIdx.x, rb = t & 7, db = t >> 3;
+    if (t < D) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + rb * 8 + i;
+        v[i] = r < seq ? *reinterpret_cast<const uint4*>(src + (int64_t)r * ld + db * 8)
+                       : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* dst) const {
+    const int t = threadIdx.x, rb = t & 7, db = t >> 3;
+    if (t < D) {
+      uint4 out[8];
+      transpose8x8(v, out);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd)
+        *reinterpret_cast<uint4*>(dst + (db * 8 + dd) * kTLD + rb * 8) = out[dd];
+    }
+  }
+};
+
+template <class Tile>
+__device__ __forceinline__ void stage(bf16_t* dst, const bf16_t* src, int64_t ld, int r0, int seq) {
+  Tile t;
+  t.load(src, ld, r0, seq);
+  t.store(dst);
 }
 
 // ------------------------------------------------------------------ forward
@@ -140,13 +168,25 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   const int qlast = min(q0 + kBQ, S) - 1;
   const int kt_lo = max(0, q0 - W + 1) / kBKV, kt_hi = qlast / kBKV;
   const bool wave_live = qw < S;
+  // tile kt + 1 is loaded into registers while tile kt is multiplied
+  RowTile<D> kreg, klreg;
+  RowTileT<D> vreg;
+  const bf16_t* Klp = SPLIT ? lo_base + A + h * D : nullptr;
+  kreg.load(Kp, ldq, kt_lo * kBKV, S);
+  if (SPLIT) klreg.load(Klp, ldl, kt_lo * kBKV, S);
+  vreg.load(Vp, ldq, kt_lo * kBKV, S);
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int j0 = kt * kBKV;
     __syncthreads();
-    stage_rows<D>(Ks, Kp, ldq, j0, S);
-    if (SPLIT) stage_rows<D>(Ks_lo, lo_base + A + h * D, ldl, j0, S);
-    stage_rows_t<D>(Vt, Vp, ldq, j0, S);
+    kreg.store(Ks);
+    if (SPLIT) klreg.store(Ks_lo);
+    vreg.store(Vt);
     __syncthreads();
+    if (kt < kt_hi) {
+      kreg.load(Kp, ldq, j0 + kBKV, S);
+      if (SPLIT) klreg.load(Klp, ldl, j0 + kBKV, S);
+      vreg.load(Vp, ldq, j0 + kBKV, S);
+    }
     if (!wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) continue;
     const bool full = (j0 + kBKV - 1 <= qw) && (qw + 31 - j0 < W) && (j0 + kBKV <= S);
     f32x16_t st[2];
@@ -299,11 +339,13 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
   for (int qt = qt_lo; qt <= qt_hi; ++qt) {
     const int i0 = qt * kBKV;
     __syncthreads();
-    stage_rows<D>(Qs, Qp, ldq, i0, S);
-    if (SPLIT) stage_rows<D>(Qs_lo, lo_base + h * D, ldl, i0, S);
-    stage_rows<D>(dOs, dOp, ld_do, i0, S);
-    stage_rows_t<D>(Qt, Qp, ldq, i0, S);
-    stage_rows_t<D>(dOt, dOp, ld_do, i0, S);
+    // each array's loads in flight at once, then its LDS stores (one array
+    // at a time: this kernel holds dK and dV for 128 keys in registers)
+    stage<RowTile<D>>(Qs, Qp, ldq, i0, S);
+    if (SPLIT) stage<RowTile<D>>(Qs_lo, lo_base + h * D, ldl, i0, S);
+    stage<RowTile<D>>(dOs, dOp, ld_do, i0, S);
+    stage<RowTileT<D>>(Qt, Qp, ldq, i0, S);
+    stage<RowTileT<D>>(dOt, dOp, ld_do, i0, S);
     if (threadIdx.x < kBKV) {
       const int i = i0 + threadIdx.x;
       lse_s[threadIdx.x] = i < S ? lse_b[i] * kLog2e : 0.f;
@@ -421,10 +463,18 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int j0 = kt * kBKV;
     __syncthreads();
-    stage_rows<D>(Ks, Kp, ldq, j0, S);
-    if (SPLIT) stage_rows<D>(Ks_lo, lo_base + A + h * D, ldl, j0, S);
-    stage_rows<D>(Vs, Vp, ldq, j0, S);
-    stage_rows_t<D>(Kt, Kp, ldq, j0, S);
+    {  // every load of the tile in flight at once, then the LDS stores
+      RowTile<D> k, kl, v;
+      RowTileT<D> kt_;
+      k.load(Kp, ldq, j0, S);
+      if (SPLIT) kl.load(lo_base + A + h * D, ldl, j0, S);
+      v.load(Vp, ldq, j0, S);
+      kt_.load(Kp, ldq, j0, S);
+      k.store(Ks);
+      if (SPLIT) kl.store(Ks_lo);
+      v.store(Vs);
+      kt_.store(Kt);
+    }
     __syncthreads();
     if (!wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) continue;
     const bool full = (j0 + kBKV - 1 <= qw) && (qw + 31 - j0 < W) && (j0 + kBKV <= S);
