@@ -38,8 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", default="175b_w512")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the fp64 CPU oracle")
@@ -234,6 +234,8 @@ def main():
     per_stage = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
                  for i, n in enumerate(names)}
     step_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)]))
+    nfb = len(B.FWD_STAGES) + len(B.BWD_STAGES)
+    fb_each = [ev[k][0].elapsed_time(ev[k][nfb]) for k in range(args.steps)]
     fwd_ms = sum(v for n, v in per_stage.items() if n.startswith("fwd."))
     bwd_ms = sum(v for n, v in per_stage.items() if n.startswith("bwd."))
     lamb_ms = per_stage["lamb"]
@@ -268,6 +270,8 @@ def main():
                    "global_batch": cfg.batch, "seq_len": cfg.seq, "parallelism": "tp8-shard"},
         "mfu": round(value / (PEAK_BF16 / 1e12), 4),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "lamb_ms": round(lamb_ms, 4),
+        "fwd_bwd_ms_median": round(float(np.median(fb_each)), 4),
+        "fwd_bwd_ms_min": round(float(np.min(fb_each)), 4),
         "lamb_gbps": round(lb / (lamb_ms * 1e-3) / 1e9, 1),
         "lamb_hbm_frac": round(lb / (lamb_ms * 1e-3) / PEAK_HBM, 4),
         "lamb_bytes": lb, "executed_tflops": round(executed, 2),

@@ -481,7 +481,10 @@ __device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int l
 // phase each wave waits for its own loads of tile t+1 and the workgroup
 // meets at the single barrier of the tile: from then on tile t's stage is
 // free, so the fourth phase reads tile t+1's first fragments and issues the
-// loads of tile t+2 into tile t's stage, a whole tile ahead of their use.
+// A half of tile t+2's loads into tile t's stage; the B half follows in the
+// first phase of tile t+1 (issuing all 16 loads per wave in one phase
+// stalled the MFMA issue behind the address unit).  Either half has at least
+// three phases before the wait that needs it.
 // Tiles past ke load zeros (no memory traffic), so the body has no
 // branches; the loop is unrolled by the number of stages so every LDS
 // address is static, and runs whole rounds of kStages tiles (an exit inside
@@ -563,11 +566,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       db.issue(rb, st + kOpBytes, wave, t >= nk1 ? t - nk1 : t, t < ke ? g.K : 0);
     };
     bf16x8_t fa[2][4], fb[2][4];
-    auto tile = [&](char* cur, const char* nxt, int t) {
+    auto tile = [&](char* cur, char* nxt, int t) {
       fra.read(fa[1], cur, 1);
       frb.read(fb[1], cur + kOpBytes, 1);
+      issue_b(nxt, t + 1);  // second half of tile t+1's loads
       mma_step(acc, fa[0], fb[0]);
-      interleave<kReads, 16 / kReads, 0, 1>();
+      interleave<kReads, 16 / kReads, kDmaPerOp, 2>();
       fra.read(fa[0], cur, 2);
       frb.read(fb[0], cur + kOpBytes, 2);
       mma_step(acc, fa[1], fb[1]);
@@ -580,17 +584,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       wait_barrier<0>();
       fra.read(fa[0], nxt, 0);
       frb.read(fb[0], nxt + kOpBytes, 0);
-      issue_a(cur, t + 2);
-      issue_b(cur, t + 2);
+      issue_a(cur, t + 2);  // first half of tile t+2's loads
       mma_step(acc, fa[1], fb[1]);
-      interleave<kReads, 16 / kReads, kDmaPerTile, 1>();
+      interleave<kReads, 16 / kReads, kDmaPerOp, 2>();
     };
 
     issue_a(st0, kb);
     issue_b(st0, kb);
     issue_a(st1, kb + 1);
-    issue_b(st1, kb + 1);
-    wait_barrier<kDmaPerTile>();
+    wait_barrier<kDmaPerOp>();
     fra.read(fa[0], st0, 0);
     frb.read(fb[0], st0 + kOpBytes, 0);
     for (int t = kb; t < ke; t += kStages) {
