@@ -9,9 +9,10 @@
 //   backward: dcat = dy w_out                 (epilogue: split + GeLU')
 //             dw_out = dy^T cat, dw_in = dz^T xn, dxn = dz w_in
 //
-// bf16 path (gfx950 MFMA): 256x256 output tile per workgroup of 4 waves, each
-// wave a 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks with fp32
-// accumulators (all 256 AGPRs); K step 64.  Operand tiles go from memory
+// bf16 path (gfx950 MFMA): 256x256 output tile per workgroup of 8 waves (two
+// per SIMD, so one wave's LDS reads, load issue and waits overlap the
+// other's MFMAs), each wave a 128x64 sub-tile of 4x2
+// v_mfma_f32_32x32x16_bf16 blocks with 128 fp32 accumulators; K step 64.  Operand tiles go from memory
 // straight into LDS (buffer loads with the LDS bit, no register staging)
 // through a 2-stage ring: the loads of the next K tile are in flight for a
 // whole tile of MFMAs.  M/N-contiguous operands stay in that layout in LDS and are
@@ -36,7 +37,8 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kStages = 2;                    // K tiles resident in LDS (2 x 64 KB)
 constexpr int kOpBytes = BM * BK * 2;         // one operand tile, 32 KB
 constexpr int kStageBytes = 2 * kOpBytes;     // A tile, then B tile
-constexpr int kGemmThreads = 256;
+constexpr int kWaves = 8;                     // 2 per SIMD; wave grid 2 (M) x 4 (N)
+constexpr int kGemmThreads = 64 * kWaves;
 constexpr int kGroupM = 8;
 
 // --------------------------------------------------------------- epilogues
@@ -223,35 +225,44 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 template <int LAY>
 struct DmaOperand {
-  uint32_t base[kDmaPerOp];  // byte offset of this lane's piece in K tile 0
-  int kin[kDmaPerOp];        // K index of the piece inside a tile (2^30 if its row is out)
-  uint32_t kstep;            // bytes from one K tile to the next
+  // Piece i of this lane lies at base + i * istep bytes, K index kin + i * ikstep;
+  // `valid` bit i: its row exists.  (The swizzle makes kin the same for every
+  // piece of a K-contiguous tile, and the row the same for every piece of an
+  // M/N-contiguous tile.)
+  uint32_t base, istep, kstep;
+  int kin, ikstep;
+  uint32_t valid;
   __device__ __forceinline__ void init(int wave, int lane, int r0, int rows, int64_t ld) {
+    valid = 0;
+    if (LAY == kKContig) {
+      const int row = 8 * wave + (lane >> 3);   // piece 0; piece i adds 64 i rows
+      kin = 8 * ((lane & 7) ^ ((row >> 1) & 7));
+      ikstep = 0;
+      base = (uint32_t)(((int64_t)(r0 + row) * ld + kin) * 2);
+      istep = (uint32_t)(64 * ld * 2);
 #pragma unroll
-    for (int i = 0; i < kDmaPerOp; ++i) {
-      const int chunk = i * 4 + wave;  // 1 KB of LDS
-      int row, kk;
-      if (LAY == kKContig) {
-        row = 8 * chunk + (lane >> 3);
-        kk = 8 * ((lane & 7) ^ ((row >> 1) & 7));
-        base[i] = (uint32_t)(((int64_t)(r0 + row) * ld + kk) * 2);
-      } else {
-        kk = 2 * chunk + (lane >> 5);
-        const int q = lane & 31;
-        row = 8 * (2 * ((q >> 1) ^ (2 * (kk & 3))) + (q & 1));
-        base[i] = (uint32_t)(((int64_t)kk * ld + r0 + row) * 2);
-      }
-      kin[i] = r0 + row < rows ? kk : (1 << 30);
+      for (int i = 0; i < kDmaPerOp; ++i) valid |= (r0 + row + 64 * i < rows ? 1u : 0u) << i;
+      kstep = (uint32_t)(BK * 2);
+    } else {
+      kin = 2 * wave + (lane >> 5);             // piece 0; piece i adds 16 i K rows
+      ikstep = 16;
+      const int q = lane & 31;
+      const int row = 8 * (2 * ((q >> 1) ^ (2 * (kin & 3))) + (q & 1));
+      base = (uint32_t)(((int64_t)kin * ld + r0 + row) * 2);
+      istep = (uint32_t)(16 * ld * 2);
+      valid = r0 + row < rows ? (1u << kDmaPerOp) - 1 : 0u;
+      kstep = (uint32_t)(BK * ld * 2);
     }
-    kstep = LAY == kKContig ? (uint32_t)(BK * 2) : (uint32_t)(BK * ld * 2);
   }
   // K tile kt of the operand into LDS at `op`; pieces at K >= klim load zeros.
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* op, int wave, int kt,
                                         int klim) const {
+    const uint32_t b = base + (uint32_t)kt * kstep;
 #pragma unroll
     for (int i = 0; i < kDmaPerOp; ++i) {
-      const uint32_t off = kt * BK + kin[i] < klim ? base[i] + (uint32_t)kt * kstep : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(op + (i * 4 + wave) * 1024), 16,
+      const bool ok = ((valid >> i) & 1u) && kt * BK + kin + i * ikstep < klim;
+      const uint32_t off = ok ? b + (uint32_t)i * istep : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(op + (i * kWaves + wave) * 1024), 16,
                                                off, 0, 0, 0);
     }
   }
@@ -259,14 +270,14 @@ struct DmaOperand {
 
 // MFMA fragments of one K=16 step for a wave's 128 rows (4 blocks of 32):
 // lane l gets rows 32 i + l%32, K values 8 (l/32) .. +8 of the step.
-template <int LAY>
+template <int LAY, int NF, int SLICE>
 struct FragReader {
   int off[4];
   __device__ __forceinline__ void init(int lane, int wsel) {
     if (LAY == kKContig) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        off[ks] = (wsel * 128 + (lane & 31)) * 128 +
+        off[ks] = (wsel * SLICE + (lane & 31)) * 128 +
                   16 * ((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7));
     } else {
       // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
@@ -274,14 +285,15 @@ struct FragReader {
       // (e = 0..3), so lane j addresses K row j/4 at M/N offset 4 (j%4).
       const int g = lane >> 4, j = lane & 15;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        off[i] = (8 * (g >> 1) + (j >> 2)) * 512 +
-                 32 * (8 * wsel + 2 * (i ^ (j >> 2)) + (g & 1)) + 8 * (j & 3);
+      for (int i = 0; i < NF; ++i) {
+        const int pair = wsel * (SLICE / 16) + 2 * i + (g & 1);
+        off[i] = (8 * (g >> 1) + (j >> 2)) * 512 + 32 * (pair ^ (2 * (j >> 2))) + 8 * (j & 3);
+      }
     }
   }
-  __device__ __forceinline__ void read(bf16x8_t (&f)[4], const char* op, int ks) const {
+  __device__ __forceinline__ void read(bf16x8_t (&f)[NF], const char* op, int ks) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NF; ++i) {
       if (LAY == kKContig) {
         f[i] = *reinterpret_cast<const bf16x8_t*>(op + off[ks] + i * 4096);
       } else {
@@ -399,26 +411,27 @@ __device__ inline int sk_slot(const GemmArgs& g, int w, int64_t s) {
   return sk_lo(g, w) >= s ? 2 * w : 2 * w + 1;
 }
 
-// 16 MFMAs of one K=16 step: the wave's 128x128 accumulators.
-__device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
-                                         const bf16x8_t (&fb)[4]) {
+// 8 MFMAs of one K=16 step: the wave's 128x64 accumulators.
+__device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][2], const bf16x8_t (&fa)[4],
+                                         const bf16x8_t (&fb)[2]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
 }
 
 // Scheduling of one phase (masks: 0x008 MFMA, 0x020 memory read, 0x100 LDS
 // read): the 16 MFMAs, each followed by an LDS read on every RS-th one (NR in
 // all) and a memory read on every VS-th one (NV in all), closed by a full
 // scheduling barrier.
-template <int NR, int RS, int NV, int VS>
+template <int NR, int NV, int VS>
 __device__ __forceinline__ void interleave() {
-  static_assert(NR * RS <= 16 && NV * VS <= 16, "fits in one phase");
+  static_assert(NR <= 16 && NV * VS <= 8, "fits in one phase");
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i % RS == 0 && i / RS < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i + 8 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     if (i % VS == VS - 1 && i / VS < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -436,28 +449,28 @@ __device__ __forceinline__ void wait_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Epilogue of one row of four 32x32 accumulator blocks (a = acc[i][0..3]):
-// each wave stages its 32x128 strip in its own LDS area (fp32; block j at
-// word j*kStageBlk + {0,4,32,36}[j] so the row-chunk reads of the four
-// blocks fall on different banks) with a short fully unrolled loop, then
-// re-reads it as 8-column row chunks (4 rows x 128 columns per wave
-// instruction) and runs the epilogue in a rolled loop, so every lane issues
-// 16-byte stores.  Contains two workgroup barriers.
+// Epilogue of one row of two 32x32 accumulator blocks (a = acc[i][0..1]):
+// each wave stages its 32x64 strip in its own LDS area (fp32; block j at
+// word j*kStageBlk + 4j so the row-chunk reads of the two blocks fall on
+// different banks) with a short fully unrolled loop, then re-reads it as
+// 8-column row chunks (8 rows x 64 columns per wave instruction) and runs
+// the epilogue in a rolled loop, so every lane issues 16-byte stores.
+// Contains two workgroup barriers.
 constexpr int kStageRow = 36, kStageBlk = 1216;
 template <class Epi>
-__device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[4], float* stage, int row0,
+__device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* stage, int row0,
                                                int col0, int lane, int M, int N, const Epi& epi) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float* blk = stage + j * kStageBlk + (j & 1) * 4 + (j >> 1) * 32;
+  for (int j = 0; j < 2; ++j) {
+    float* blk = stage + j * kStageBlk + j * 4;
 #pragma unroll
     for (int r = 0; r < 16; ++r) blk[mfma32_row(r, lane) * kStageRow + (lane & 31)] = a[j][r];
   }
   __syncthreads();
 #pragma unroll 1
-  for (int c = lane; c < 32 * 16; c += 64) {
-    const int rr = c >> 4, jc = c & 15, j = jc >> 2, c8 = (jc & 3) * 8;
-    const float* src = stage + j * kStageBlk + (j & 1) * 4 + (j >> 1) * 32 + rr * kStageRow + c8;
+  for (int c = lane; c < 32 * 8; c += 64) {
+    const int rr = c >> 3, jc = c & 7, j = jc >> 2, c8 = (jc & 3) * 8;
+    const float* src = stage + j * kStageBlk + j * 4 + rr * kStageRow + c8;
     const float4 lo = *reinterpret_cast<const float4*>(src);
     const float4 hi = *reinterpret_cast<const float4*>(src + 4);
     const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -471,7 +484,7 @@ __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[4], float* st
 // a partial tile: one 1 KB run per (wave, i, j, r4), so each store or load
 // instruction of a wave is contiguous.
 __device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int lane) {
-  return ((((wave * 4 + i) * 4 + j) * 4 + r4) * 64 + lane) * 4;
+  return ((((wave * 4 + i) * 2 + j) * 4 + r4) * 64 + lane) * 4;
 }
 
 // Main loop of one segment (K iterations kb .. ke of a tile): a two-stage
@@ -502,13 +515,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   const __amdgpu_buffer_rsrc_t ra2 = make_rsrc(g.a2 != nullptr ? g.a2 : g.a, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, g.b_bytes);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  FragReader<ALAY> fra;
-  FragReader<BLAY> frb;
+  const int wm = wave >> 2, wn = wave & 3;
+  FragReader<ALAY, 4, 128> fra;
+  FragReader<BLAY, 2, 64> frb;
   fra.init(lane, wm);
   frb.init(lane, wn);
-  float* stage = reinterpret_cast<float*>((wave < 2 ? st0 : st1) + (wave & 1) * (kStageBytes / 2));
-  constexpr int kReads = (ALAY == kKContig ? 4 : 8) + (BLAY == kKContig ? 4 : 8);
+  float* stage = reinterpret_cast<float*>((wave < 4 ? st0 : st1) + (wave & 3) * (2 * kStageBlk * 4));
+  static_assert(4 * 2 * kStageBlk * 4 <= kStageBytes, "epilogue staging");
+  constexpr int kReads = (ALAY == kKContig ? 4 : 8) + (BLAY == kKContig ? 2 : 4);
   const int nk1 = g.sc.nk1;
 
   // segment source: whole tiles first, then (sk) this worker's range
@@ -550,11 +564,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     DmaOperand<BLAY> db;
     da.init(wave, lane, m0, g.M, g.lda);
     db.init(wave, lane, n0, g.N, g.ldb);
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -565,28 +579,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     auto issue_b = [&](char* st, int t) {
       db.issue(rb, st + kOpBytes, wave, t >= nk1 ? t - nk1 : t, t < ke ? g.K : 0);
     };
-    bf16x8_t fa[2][4], fb[2][4];
+    bf16x8_t fa[2][4], fb[2][2];
     auto tile = [&](char* cur, char* nxt, int t) {
       fra.read(fa[1], cur, 1);
       frb.read(fb[1], cur + kOpBytes, 1);
       issue_b(nxt, t + 1);  // second half of tile t+1's loads
       mma_step(acc, fa[0], fb[0]);
-      interleave<kReads, 16 / kReads, kDmaPerOp, 2>();
+      interleave<kReads, kDmaPerOp, 2>();
       fra.read(fa[0], cur, 2);
       frb.read(fb[0], cur + kOpBytes, 2);
       mma_step(acc, fa[1], fb[1]);
-      interleave<kReads, 16 / kReads, 0, 1>();
+      interleave<kReads, 0, 1>();
       fra.read(fa[1], cur, 3);
       frb.read(fb[1], cur + kOpBytes, 3);
       mma_step(acc, fa[0], fb[0]);
-      interleave<kReads, 16 / kReads, 0, 1>();
+      interleave<kReads, 0, 1>();
       // tile t+1 has landed and every wave is done reading tile t
       wait_barrier<0>();
       fra.read(fa[0], nxt, 0);
       frb.read(fb[0], nxt + kOpBytes, 0);
       issue_a(cur, t + 2);  // first half of tile t+2's loads
       mma_step(acc, fa[1], fb[1]);
-      interleave<kReads, 16 / kReads, kDmaPerOp, 2>();
+      interleave<kReads, kDmaPerOp, 2>();
     };
 
     issue_a(st0, kb);
@@ -605,13 +619,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     if (slot < 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        epilogue_strip(acc[i], stage, m0 + wm * 128 + i * 32, n0 + wn * 128, lane, g.M, g.N, epi);
+        epilogue_strip(acc[i], stage, m0 + wm * 128 + i * 32, n0 + wn * 64, lane, g.M, g.N, epi);
     } else {
       float* p = g.ws + (size_t)slot * kPartialFloats;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4)
             *reinterpret_cast<float4*>(p + partial_off(wave, i, j, r4, lane)) =
@@ -628,7 +642,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 // their loads are in flight together.
 template <class Epi>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fixup_kernel(GemmArgs g, Epi epi) {
-  __shared__ __attribute__((aligned(16))) float stage_all[4][4 * kStageBlk];
+  __shared__ __attribute__((aligned(16))) float stage_all[kWaves][2 * kStageBlk];
   const int l = g.dp_tiles + (blockIdx.x >> 2), i = blockIdx.x & 3;
   const int64_t s = g.sc.start(l), e = g.sc.start(l + 1);
   const int w0 = sk_owner(g, s), w1 = sk_owner(g, e - 1);
@@ -636,10 +650,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fixup_kernel(GemmArgs g, Ep
   int tm, tn;
   g.sc.tile(l, tm, tn);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x16_t a[4];
+  const int wm = wave >> 2, wn = wave & 3;
+  f32x16_t a[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) a[j][r] = 0.f;
 #pragma unroll 1
@@ -649,18 +663,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fixup_kernel(GemmArgs g, Ep
     int n = 0;
     for (; w <= w1 && n < 2; ++w)
       if (sk_lo(g, w) != sk_lo(g, w + 1)) src[n++] = g.ws + (size_t)sk_slot(g, w, s) * kPartialFloats;
-    float4 v[2][16];
+    float4 v[2][8];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       if (q < n)
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
+        for (int c = 0; c < 8; ++c)
           v[q][c] = *reinterpret_cast<const float4*>(src[q] + partial_off(wave, i, c >> 2, c & 3, lane));
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       if (q < n)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
+        for (int c = 0; c < 8; ++c) {
           f32x16_t& t = a[c >> 2];
           const int r = 4 * (c & 3);
           t[r] += v[q][c].x;
@@ -669,7 +683,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fixup_kernel(GemmArgs g, Ep
           t[r + 3] += v[q][c].w;
         }
   }
-  epilogue_strip(a, stage_all[wave], tm * BM + wm * 128 + i * 32, tn * BN + wn * 128, lane, g.M,
+  epilogue_strip(a, stage_all[wave], tm * BM + wm * 128 + i * 32, tn * BN + wn * 64, lane, g.M,
                  g.N, epi);
 }
 
