@@ -28,7 +28,8 @@ def _rand(rng, shape, dtype, scale=1.0):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("rows,width", [(1, 8), (37, 264), (130, 4104), (64, 12288), (3, 32768)])
+@pytest.mark.parametrize("rows,width", [(1, 8), (37, 264), (130, 4104), (64, 12288), (3, 32768),
+                                        (2500, 264), (1100, 20480)])
 def test_layernorm_forward(dtype, rows, width):
     print(f"layernorm {dtype} rows={rows} width={width}", flush=True)
     rng = np.random.default_rng(rows * 7 + width)

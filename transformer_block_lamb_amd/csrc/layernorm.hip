@@ -25,6 +25,150 @@ constexpr int kLnThreads = 512;
 constexpr int kLnWaves = kLnThreads / 64;
 constexpr int kRowsPerBlock = 8;
 
+// Loads one row's NV 16-byte vectors per thread (zeros past the width).
+template <typename T, int NV>
+__device__ __forceinline__ void load_row(const T* r, int nvec, float (&v)[NV][8]) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = threadIdx.x + kLnThreads * i;
+    if (vi < nvec) {
+      Vec8<T>::load(r + vi * 8, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    }
+  }
+}
+
+// Eight values kept as loaded (bf16 stays packed, halving the registers a
+// prefetched row needs); get() widens them to fp32.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void get(float (&o)[8]) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void get(float (&o)[8]) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+template <typename T, int NV>
+__device__ __forceinline__ void load_raw(const T* r, int nvec, Raw8<T> (&v)[NV]) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = threadIdx.x + kLnThreads * i;
+    if (vi < nvec) v[i].load(r + vi * 8); else v[i].zero();
+  }
+}
+
+// ROWS_PER_BLOCK consecutive rows per workgroup; the next row's x, dxn and
+// dy are loaded while the current row is reduced (launched while those
+// registers fit: up to 3 vectors per thread for bf16 rows, 2 for fp32).
+template <typename T, int NV>
+__global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(
+    const T* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const float* __restrict__ dxn, const T* __restrict__ dy,
+    T* __restrict__ dx, float* __restrict__ gpart, float* __restrict__ bpart, int rows,
+    int width) {
+  __shared__ float red[kLnWaves];
+  const int nvec = width >> 3;
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int rend = min(rows, r0 + kRowsPerBlock);
+  const float inv_w = 1.0f / (float)width;
+  float ag[NV][8], ab[NV][8], gm[NV][8];
+  load_row<float, NV>(gamma, nvec, gm);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { ag[i][e] = 0.f; ab[i][e] = 0.f; }
+  Raw8<T> xr[NV], yr[NV], nxr[NV], nyr[NV];
+  Raw8<float> dr[NV], ndr[NV];
+  if (r0 < rend) {
+    load_raw<T, NV>(x + (int64_t)r0 * width, nvec, xr);
+    load_raw<float, NV>(dxn + (int64_t)r0 * width, nvec, dr);
+    if (dy != nullptr) load_raw<T, NV>(dy + (int64_t)r0 * width, nvec, yr);
+  }
+  for (int row = r0; row < rend; ++row) {  // uniform over the block
+    if (row + 1 < rend) {
+      load_raw<T, NV>(x + (int64_t)(row + 1) * width, nvec, nxr);
+      load_raw<float, NV>(dxn + (int64_t)(row + 1) * width, nvec, ndr);
+      if (dy != nullptr) load_raw<T, NV>(dy + (int64_t)(row + 1) * width, nvec, nyr);
+    }
+    const float mu = mean[row], rs = rstd[row];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool in = threadIdx.x + kLnThreads * i < nvec;
+      float xv[8], dv[8];
+      xr[i].get(xv);
+      dr[i].get(dv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xh = in ? (xv[e] - mu) * rs : 0.f;
+        const float dxh = dv[e] * gm[i][e];
+        s1 += dxh;
+        s2 += dxh * xh;
+        ag[i][e] += dv[e] * xh;
+        ab[i][e] += dv[e];
+      }
+    }
+    const float m1 = block_sum<kLnWaves>(s1, red) * inv_w;
+    const float m2 = block_sum<kLnWaves>(s2, red) * inv_w;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = threadIdx.x + kLnThreads * i;
+      if (vi < nvec) {
+        float xv[8], dv[8], o[8];
+        xr[i].get(xv);
+        dr[i].get(dv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (xv[e] - mu) * rs;
+          o[e] = rs * (dv[e] * gm[i][e] - m1 - xh * m2);
+        }
+        if (dy != nullptr) {
+          float yv[8];
+          yr[i].get(yv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += yv[e];
+        }
+        Vec8<T>::store(dx + (int64_t)row * width + vi * 8, o);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      xr[i] = nxr[i];
+      dr[i] = ndr[i];
+      yr[i] = nyr[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = threadIdx.x + kLnThreads * i;
+    if (vi < nvec) {
+      Vec8<float>::store(gpart + (int64_t)blockIdx.x * width + vi * 8, ag[i]);
+      Vec8<float>::store(bpart + (int64_t)blockIdx.x * width + vi * 8, ab[i]);
+    }
+  }
+}
+
+// Forward: one workgroup per row.
 template <typename T, int NV>
 __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict__ x,
                                                             const float* __restrict__ gamma,
@@ -92,8 +236,10 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict_
   }
 }
 
+// Backward for wider rows: the same arithmetic, one row at a time without
+// the next-row loads.
 template <typename T, int NV>
-__global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(
+__global__ __launch_bounds__(kLnThreads) void ln_bwd_plain_kernel(
     const T* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ dxn, const T* __restrict__ dy,
     T* __restrict__ dx, float* __restrict__ gpart, float* __restrict__ bpart, int rows,
@@ -227,8 +373,16 @@ hipError_t bwd_nv(const void* x, const float* gamma, const float* mean, const fl
                   const float* dxn, const void* dy, void* dx, float* gp, float* bp, int rows,
                   int width, hipStream_t s) {
   const int nblk = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(nblk), dim3(kLnThreads), 0, s, (const T*)x,
-                     gamma, mean, rstd, dxn, (const T*)dy, (T*)dx, gp, bp, rows, width);
+  // the prefetched row fits in registers up to 3 vectors per thread for
+  // bf16 rows, 2 for fp32 rows
+  if constexpr (NV <= (sizeof(T) == 2 ? 3 : 2))
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(nblk), dim3(kLnThreads), 0, s,
+                       (const T*)x, gamma, mean, rstd, dxn, (const T*)dy, (T*)dx, gp, bp, rows,
+                       width);
+  else
+    hipLaunchKernelGGL((ln_bwd_plain_kernel<T, NV>), dim3(nblk), dim3(kLnThreads), 0, s,
+                       (const T*)x, gamma, mean, rstd, dxn, (const T*)dy, (T*)dx, gp, bp, rows,
+                       width);
   return hipGetLastError();
 }
 
