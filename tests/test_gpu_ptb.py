@@ -19,6 +19,12 @@ RAGGED = [
     PtbConfig("ragged_w1", 1, 130, 256, 2, 64, 256, 1, "bf16", 1),
     PtbConfig("tiny_bf16", 1, 128, 256, 4, 64, 1024, 32, "bf16", 1),
     PtbConfig("ragged_f32", 2, 77, 72, 2, 64, 40, 20, "f32", 1),
+    # input projections with two-pass (q, k) tiles under the split-K
+    # schedules on 256 CUs: single-pass tiles whole, then the two-pass ones
+    # split (1800 tokens: 8 M-tiles, the last ragged); all tiles split
+    # (1000 tokens, K = 1000 not a multiple of the 64-wide K tile)
+    PtbConfig("sk_lf_ragged", 1, 1800, 1024, 3, 128, 7096, 300, "bf16", 1),
+    PtbConfig("sk_pure_ragged", 1, 1000, 1000, 3, 128, 8000, 100, "bf16", 1),
 ]
 
 

@@ -307,56 +307,77 @@ struct FragReader {
 };
 
 // --------------------------------------------------------------- schedule
-// Logical tile order: groups of kGroupM M-tiles, M-fastest within a group.
-// The first nh N-tiles also run the a2 pass (2 nk1 K iterations instead of
-// nk1).  start(l) is the first iteration of logical tile l in the
+// Logical tile order: groups of gm M-tiles, M-fastest within a group, over
+// logical N columns.  The first nh physical N-tiles also run the a2 pass
+// (2 nk1 K iterations instead of nk1).  With light_first the logical columns
+// list the single-pass columns first (physical nh .. ntn-1, then 0 .. nh-1),
+// so that with one group (gm = ntm) every single-pass tile precedes every
+// two-pass tile.  start(l) is the first iteration of logical tile l in the
 // concatenation of all tiles' K iterations; locate() inverts it.
 struct Sched {
-  int ntm, ntn, nk1, nh;
+  int ntm, ntn, nk1, nh, gm, light_first;
+  // K iterations of physical N-tile tn
   __host__ __device__ int cost(int tn) const { return tn < nh ? 2 * nk1 : nk1; }
-  __host__ __device__ int64_t col_prefix(int tn) const {
-    return (int64_t)nk1 * (tn + (tn < nh ? tn : nh));
+  __host__ __device__ int phys(int c) const {
+    return !light_first ? c : (c < ntn - nh ? c + nh : c - (ntn - nh));
+  }
+  // iterations of one M-tile row over logical columns [0, c)
+  __host__ __device__ int64_t col_prefix(int c) const {
+    if (light_first) {
+      const int extra = c - (ntn - nh);
+      return (int64_t)nk1 * (c + (extra > 0 ? extra : 0));
+    }
+    return (int64_t)nk1 * (c + (c < nh ? c : nh));
   }
   __host__ __device__ int group_size(int first_m) const {
-    return ntm - first_m < kGroupM ? ntm - first_m : kGroupM;
+    return ntm - first_m < gm ? ntm - first_m : gm;
+  }
+  __host__ __device__ void logical(int l, int& tm, int& c) const {
+    const int group = l / (gm * ntn), first_m = group * gm;
+    const int gsize = group_size(first_m), in = l - group * gm * ntn;
+    c = in / gsize;
+    tm = first_m + in % gsize;
   }
   __host__ __device__ void tile(int l, int& tm, int& tn) const {
-    const int group = l / (kGroupM * ntn), first_m = group * kGroupM;
-    const int gsize = group_size(first_m), in = l - group * kGroupM * ntn;
-    tn = in / gsize;
-    tm = first_m + in % gsize;
+    int c;
+    logical(l, tm, c);
+    tn = phys(c);
   }
   __host__ __device__ int64_t start(int l) const {
     if (l >= ntm * ntn) return (int64_t)ntm * col_prefix(ntn);
-    int tm, tn;
-    tile(l, tm, tn);
-    const int first_m = tm - tm % kGroupM;
-    return (int64_t)first_m * col_prefix(ntn) + (int64_t)group_size(first_m) * col_prefix(tn) +
-           (int64_t)(tm - first_m) * cost(tn);
+    int tm, c;
+    logical(l, tm, c);
+    const int first_m = tm - tm % gm;
+    return (int64_t)first_m * col_prefix(ntn) + (int64_t)group_size(first_m) * col_prefix(c) +
+           (int64_t)(tm - first_m) * cost(phys(c));
   }
   __host__ __device__ void locate(int64_t it, int& l, int& koff) const {
     const int64_t row = col_prefix(ntn);
-    const int ngroups = (ntm + kGroupM - 1) / kGroupM;
-    int group = (int)(it / (kGroupM * row));
+    const int ngroups = (ntm + gm - 1) / gm;
+    int group = (int)(it / (gm * row));
     if (group >= ngroups) group = ngroups - 1;
-    const int first_m = group * kGroupM, gsize = group_size(first_m);
+    const int first_m = group * gm, gsize = group_size(first_m);
     int64_t rem = it - (int64_t)first_m * row;
-    const int64_t heavy = (int64_t)gsize * 2 * nk1 * nh;
-    int tn, c;
-    if (rem < heavy) {
-      c = 2 * nk1;
-      tn = (int)(rem / ((int64_t)gsize * c));
-      rem -= (int64_t)tn * gsize * c;
+    // the logical columns form two runs of equal cost: n0 columns of c0
+    // iterations, then the rest of c1
+    const int n0 = light_first ? ntn - nh : nh;
+    const int c0 = light_first ? nk1 : 2 * nk1, c1 = light_first ? 2 * nk1 : nk1;
+    const int64_t first_run = (int64_t)gsize * c0 * n0;
+    int c, cost_c;
+    if (rem < first_run) {
+      cost_c = c0;
+      c = (int)(rem / ((int64_t)gsize * c0));
+      rem -= (int64_t)c * gsize * c0;
     } else {
-      c = nk1;
-      rem -= heavy;
-      const int q = (int)(rem / ((int64_t)gsize * c));
-      tn = nh + q;
-      rem -= (int64_t)q * gsize * c;
+      cost_c = c1;
+      rem -= first_run;
+      const int q = (int)(rem / ((int64_t)gsize * c1));
+      c = n0 + q;
+      rem -= (int64_t)q * gsize * c1;
     }
-    const int r = (int)(rem / c);
-    koff = (int)(rem - (int64_t)r * c);
-    l = group * kGroupM * ntn + tn * gsize + r;
+    const int r = (int)(rem / cost_c);
+    koff = (int)(rem - (int64_t)r * cost_c);
+    l = group * gm * ntn + c * gsize + r;
   }
 };
 
@@ -528,8 +549,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   // segment source: whole tiles first, then (sk) this worker's range
   const int b = blockIdx.x, per = g.grid >> 3;
   const int gl = (b & 7) * per + (b >> 3);  // sk: XCD-contiguous worker index
-  int dp_left = g.sk ? g.dp_tiles / g.grid : 1;
-  int dp_next = (b & 7) * (g.dp_tiles >> 3) + (b >> 3);
+  // sk: XCD x owns logical tiles [x dpx, (x + 1) dpx) of the whole-tile
+  // part; its workers take them round-robin
+  const int dpx = g.dp_tiles >> 3, local = b >> 3;
+  int dp_left = !g.sk ? 1 : (local < dpx ? (dpx - local + per - 1) / per : 0);
+  int dp_next = (b & 7) * dpx + local;
   int64_t it = g.sk ? sk_lo(g, gl) : 0;
   const int64_t it_end = g.sk ? sk_lo(g, gl + 1) : 0;
   bool first_sk = true;
@@ -779,7 +803,7 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
   g.b_bytes = (uint32_t)(b_elems * 2);
   const int ntm = (d.M + BM - 1) / BM, ntn = (d.N + BN - 1) / BN;
   const int nh = d.a2 != nullptr ? min(ntn, (d.n_split + BN - 1) / BN) : 0;
-  g.sc = Sched{ntm, ntn, (d.K + BK - 1) / BK, nh};
+  g.sc = Sched{ntm, ntn, (d.K + BK - 1) / BK, nh, kGroupM, 0};
   const int tiles = ntm * ntn;
   g.ws = static_cast<float*>(d.ws);
   g.use_perm = 0;
@@ -791,16 +815,36 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
   // Stream-K when whole tiles per CU would leave more than a tenth of the
   // machine idle: compare the ideal share of K iterations per CU with the
   // busiest CU of the one-tile-per-workgroup schedule (a two-pass tile
-  // counts twice).
+  // counts twice, and alone takes two units).
   const int G = persistent_grid();
   const int64_t total = g.sc.start(tiles);
   if (G >= 8 && g.ws != nullptr && d.ws_bytes >= kGemmWsBytes && total >= 2 * (int64_t)G * kStages) {
-    const int64_t units = tiles + (int64_t)nh * ntm;  // in light-tile units
-    const int64_t dp_time = ((units + G - 1) / G) * g.sc.nk1;
+    const int64_t units = tiles + (int64_t)nh * ntm;  // in single-pass-tile units
+    int64_t dp_rounds = (units + G - 1) / G;
+    if (nh > 0 && dp_rounds < 2) dp_rounds = 2;
+    const int64_t dp_time = dp_rounds * g.sc.nk1;
     if ((double)total / G < 0.9 * (double)dp_time) {
       g.sk = 1;
       g.grid = G;
-      g.dp_tiles = nh == 0 ? (tiles / G) * G : 0;
+      g.dp_tiles = (tiles / G) * G;  // whole waves of tiles, the remainder split
+      if (nh > 0) {
+        // Single-pass tiles first, whole (their loads stay aligned across the
+        // CUs of an XCD, so they share operand panels in L2), the two-pass
+        // tiles split over all CUs; taken when its busiest CU is within a
+        // tenth of the even split of everything.
+        Sched lf = g.sc;
+        lf.light_first = 1;
+        lf.gm = ntm;
+        const int dp = (ntm * (ntn - nh)) & ~7;
+        const int64_t per = G / 8, dpx = dp / 8;
+        const int64_t busiest = (dpx + per - 1) / per * lf.nk1 + (total - lf.start(dp)) / G;
+        if ((double)busiest <= 1.1 * (double)total / G) {
+          g.sc = lf;
+          g.dp_tiles = dp;
+        } else {
+          g.dp_tiles = 0;
+        }
+      }
       g.sk_base = g.sc.start(g.dp_tiles);
       g.sk_iters = total - g.sk_base;
     }
