@@ -514,11 +514,10 @@ __device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int l
 // reads the next step's fragments while it multiplies.  After the third
 // phase each wave waits for its own loads of tile t+1 and the workgroup
 // meets at the single barrier of the tile: from then on tile t's stage is
-// free, so the fourth phase reads tile t+1's first fragments and issues the
-// A half of tile t+2's loads into tile t's stage; the B half follows in the
-// first phase of tile t+1 (issuing all 16 loads per wave in one phase
-// stalled the MFMA issue behind the address unit).  Either half has at least
-// three phases before the wait that needs it.
+// free, so the fourth phase reads tile t+1's first fragments and issues
+// tile t+2's loads into tile t's stage, a whole tile ahead of their use (for
+// an M/N-contiguous A only the A half; the B half follows in the first phase
+// of tile t+1).
 // Tiles past ke load zeros (no memory traffic), so the body has no
 // branches; the loop is unrolled by the number of stages so every LDS
 // address is static, and runs whole rounds of kStages tiles (an exit inside
@@ -544,6 +543,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   float* stage = reinterpret_cast<float*>((wave < 4 ? st0 : st1) + (wave & 3) * (2 * kStageBlk * 4));
   static_assert(4 * 2 * kStageBlk * 4 <= kStageBytes, "epilogue staging");
   constexpr int kReads = (ALAY == kKContig ? 4 : 8) + (BLAY == kKContig ? 2 : 4);
+  // When to issue tile t+2's loads (measured per layout): all right after
+  // the barrier of tile t when A is K-contiguous; for an M/N-contiguous A the
+  // B half one phase later, which spreads the issue.
+  constexpr bool kSplitIssue = ALAY == kMNContig;
   const int nk1 = g.sc.nk1;
 
   // segment source: whole tiles first, then (sk) this worker's range
@@ -607,9 +610,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     auto tile = [&](char* cur, char* nxt, int t) {
       fra.read(fa[1], cur, 1);
       frb.read(fb[1], cur + kOpBytes, 1);
-      issue_b(nxt, t + 1);  // second half of tile t+1's loads
-      mma_step(acc, fa[0], fb[0]);
-      interleave<kReads, kDmaPerOp, 2>();
+      if constexpr (kSplitIssue) {
+        issue_b(nxt, t + 1);  // second half of tile t+1's loads
+        mma_step(acc, fa[0], fb[0]);
+        interleave<kReads, kDmaPerOp, 2>();
+      } else {
+        mma_step(acc, fa[0], fb[0]);
+        interleave<kReads, 0, 1>();
+      }
       fra.read(fa[0], cur, 2);
       frb.read(fb[0], cur + kOpBytes, 2);
       mma_step(acc, fa[1], fb[1]);
@@ -622,15 +630,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       wait_barrier<0>();
       fra.read(fa[0], nxt, 0);
       frb.read(fb[0], nxt + kOpBytes, 0);
-      issue_a(cur, t + 2);  // first half of tile t+2's loads
-      mma_step(acc, fa[1], fb[1]);
-      interleave<kReads, kDmaPerOp, 2>();
+      issue_a(cur, t + 2);  // tile t+2's loads (with kSplitIssue: the A half)
+      if constexpr (kSplitIssue) {
+        mma_step(acc, fa[1], fb[1]);
+        interleave<kReads, kDmaPerOp, 2>();
+      } else {
+        issue_b(cur, t + 2);
+        mma_step(acc, fa[1], fb[1]);
+        interleave<kReads, kDmaPerTile, 1>();
+      }
     };
 
     issue_a(st0, kb);
     issue_b(st0, kb);
     issue_a(st1, kb + 1);
-    wait_barrier<kDmaPerOp>();
+    if constexpr (kSplitIssue) {
+      wait_barrier<kDmaPerOp>();
+    } else {
+      issue_b(st1, kb + 1);
+      wait_barrier<kDmaPerTile>();
+    }
     fra.read(fa[0], st0, 0);
     frb.read(fb[0], st0 + kOpBytes, 0);
     for (int t = kb; t < ke; t += kStages) {
