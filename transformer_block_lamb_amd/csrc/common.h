@@ -77,6 +77,11 @@ template <> struct Vec8<float> {
 // A raw buffer resource: loads whose byte offset lies at or beyond
 // `bytes` return zeros (hardware range check), so tile loaders mask a ragged
 // edge by steering the offset out of range instead of branching.
+// LDS (address space 3) pointer types for the LDS-bound buffer loads and
+// the transposing LDS reads.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kBufferFlags = 0x00020000;  // gfx9 data format word of the descriptor
 

@@ -220,8 +220,6 @@ __device__ __forceinline__ void tile_coords(int bid, int ntm, int ntn, const int
 constexpr int kDmaPerOp = kOpBytes / (kGemmThreads * 16);  // DMA instructions per lane
 constexpr int kDmaPerTile = 2 * kDmaPerOp;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 template <int LAY>
 struct DmaOperand {

@@ -13,9 +13,13 @@
 //     query: the online softmax (running max and sum, base-2 exponent) then
 //     needs a single lane exchange, and the probabilities already sit in
 //     the B-operand layout of O^T += V^T P^T (keys reordered inside the K=16
-//     step, the same order used to read V^T from LDS).  V is transposed in
-//     registers (8x8 blocks) on its way into LDS.  The log-sum-exp of each
-//     query is written for the backward.
+//     step, the same order used to read V^T from LDS).  The log-sum-exp of
+//     each query is written for the backward.
+//   * every key/query tile moves from memory straight into LDS (row-major,
+//     LDS-bound buffer loads, double-buffered so the next tile loads while
+//     the current one is multiplied); the transposed operands (V^T, dO^T,
+//     Q^T, K^T) are read from those row-major tiles with the transposing
+//     LDS read, so no transposed copy is ever staged.
 //   * backward (FlashAttention-2 style, no atomics, deterministic):
 //     D_i = dO_i . O_i; then one kernel per 128-key block accumulates dK and
 //     dV over the query tiles of the band (S = Q K^T, P = exp(S - lse),
@@ -33,19 +37,9 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBQ = 128, kBKV = 64, kSwaThreads = 256;
-constexpr int kTLD = kBKV + 8;  // row stride (elements) of transposed LDS tiles
 
 __device__ __forceinline__ bf16x8_t ld_frag(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
-}
-// A-operand fragment of a transposed tile whose K index is the reordered
-// key/query order used for probabilities held in MFMA output layout: lane l
-// takes elements [base + 4*(l/32) + 0..3] and [base + 8 + 4*(l/32) + 0..3].
-__device__ __forceinline__ bf16x8_t ld_frag_reordered(const bf16_t* row, int lane) {
-  const bf16_t* p = row + 4 * (lane >> 5);
-  const uint2 lo = *reinterpret_cast<const uint2*>(p);
-  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
-  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 __device__ __forceinline__ bf16x8_t pack8(const float* v) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]),
@@ -53,66 +47,85 @@ __device__ __forceinline__ bf16x8_t pack8(const float* v) {
 }
 __device__ __forceinline__ bool visible(int i, int j, int w) { return j <= i && i - j < w; }
 
-// Register-staged copies of one 64-row tile, so the loads of the next tile
-// can be issued before the current one is consumed: load() issues every
-// global load of this thread's share at once, store() writes it to LDS.
-// RowTile: rows [r0, r0 + 64) x D into LDS row-major (stride D + 8); thread
-// t owns 16-byte chunks t, t + 256, ... (D / 32 of them).
+// LDS row stride (elements) of a 64-row tile of D columns: D plus a pad
+// chosen so that the fragment reads of consecutive rows fall on distinct
+// banks, both the 16-byte row reads (8 rows at a time) and the transposing
+// 8-byte reads (4 rows of 32 bytes at a time): the stride in 4-byte banks is
+// 36, 52 and 72 for D = 64, 96 and 128.
 template <int D>
-struct RowTile {
-  static constexpr int CH = D / 8, N = kBKV * CH / kSwaThreads;
-  static_assert(N * kSwaThreads == kBKV * CH, "whole chunks per thread");
-  uint4 v[N];
-  __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int r0, int seq) {
+constexpr int kTileLd = D + (D == 128 ? 16 : 8);
+
+// One 64-row tile (rows r0 .. r0 + 63 of a token-major matrix, D columns)
+// goes from memory straight into LDS with buffer loads that carry the LDS
+// bit: one wave instruction writes 1 KB of LDS, lane L's 16 bytes at byte
+// 16 L, so the row-major LDS tile (kTileLd<D> elements per row) is covered
+// by SL = kTileLd<D> / 8 instructions.  Lanes that land on a pad slot, or
+// on a row at or beyond `lim`, are steered out of the buffer's range and
+// write zeros.  Instruction n is issued by wave n % 4; slot[k] packs the
+// row (bits 5..) and 16-byte column (bits 0..4) of this lane's piece of
+// instruction wave + 4k, with pad slots pushed past every row limit.
+template <int D>
+struct DmaRows {
+  static constexpr int CH = D / 8, SL = kTileLd<D> / 8;
+  static constexpr int NI = SL;             // 1 KB instructions per tile
+  static constexpr int NW = (NI + 3) / 4;   // per wave, at most
+  int slot[NW];
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = threadIdx.x + i * kSwaThreads, r = c / CH, cc = c - r * CH;
-      v[i] = r0 + r < seq ? *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * ld + cc * 8)
-                          : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < NW; ++k) {
+      const int s = (wave + 4 * k) * 64 + lane, r = s / SL, c = s - r * SL;
+      slot[k] = c < CH ? (r << 5) | c : (1 << 30);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* dst) const {
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, bf16_t* tile, int wave, int r0,
+                                        int lim, int64_t ld) const {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = threadIdx.x + i * kSwaThreads, r = c / CH, cc = c - r * CH;
-      *reinterpret_cast<uint4*>(dst + r * (D + 8) + cc * 8) = v[i];
-    }
-  }
-};
-// RowTileT: the same rows stored transposed, dst[dim][row] with stride kTLD;
-// thread t < D owns the 8-row x 8-dim block (rows 8 (t & 7), dims 8 (t >> 3))
-// and transposes it in registers.
-template <int D>
-struct RowTileT {
-  uint4 v[8];
-  __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int r0, int seq) {
-    const int t = threadIdx.x, rb = t & 7, db = t >> 3;
-    if (t < D) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = r0 + rb * 8 + i;
-        v[i] = r < seq ? *reinterpret_cast<const uint4*>(src + (int64_t)r * ld + db * 8)
-                       : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < NW; ++k) {
+      const int n = wave + 4 * k;
+      if (n < NI) {  // uniform over the wave
+        const int r = r0 + (slot[k] >> 5);
+        const uint32_t o = r < lim ? (uint32_t)r * (uint32_t)(ld * 2) + 16u * (slot[k] & 31)
+                                   : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + n * 512), 16, o, 0, 0,
+                                                 0);
       }
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* dst) const {
-    const int t = threadIdx.x, rb = t & 7, db = t >> 3;
-    if (t < D) {
-      uint4 out[8];
-      transpose8x8(v, out);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd)
-        *reinterpret_cast<uint4*>(dst + (db * 8 + dd) * kTLD + rb * 8) = out[dd];
     }
   }
 };
 
-template <class Tile>
-__device__ __forceinline__ void stage(bf16_t* dst, const bf16_t* src, int64_t ld, int r0, int seq) {
-  Tile t;
-  t.load(src, ld, r0, seq);
-  t.store(dst);
+// The buffer covering one sequence's rows of a D-column block: rows 0 ..
+// seq - 1 of a token-major matrix with leading dimension ld (the entry
+// points keep every token-major matrix below 2^31 bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16_t* p, int64_t ld, int seq,
+                                                            int D) {
+  return make_rsrc(p, (uint32_t)(((int64_t)(seq - 1) * ld + D) * 2));
+}
+
+// A-operand fragment of a transposed tile, read from the row-major LDS tile
+// (row stride LD) with ds_read_b64_tr_b16: M = 32 columns (dbase ..), K = 16
+// tile rows from row0 taken in the order of probabilities held in MFMA
+// output layout (MFMA K index 0-3 -> rows 0-3, 4-7 -> 8-11, 8-11 -> 4-7,
+// 12-15 -> 12-15).  In each group of 16 lanes, lane i receives element i%4
+// of the 4-value pieces addressed by lanes 4e + i/4 (e = 0..3), so lane j
+// addresses tile row 4 (g/2) + j/4 at column 16 (g%2) + 4 (j%4); the second
+// read covers the rows 8 further down.
+template <int LD>
+__device__ __forceinline__ bf16x8_t ld_frag_tr(const bf16_t* tile, int row0, int dbase, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int idx = (row0 + 4 * (g >> 1) + (j >> 2)) * LD + dbase + 16 * (g & 1) + 4 * (j & 3);
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)&tile[idx]);
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)&tile[idx + 8 * LD]);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Waits for this wave's outstanding loads (the LDS-bound ones included) and
+// LDS reads, then joins the workgroup barrier: after it every wave's tile
+// loads issued before it have landed in LDS.
+__device__ __forceinline__ void drain_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ------------------------------------------------------------------ forward
@@ -132,6 +145,12 @@ __device__ __forceinline__ void load_row_frags(bf16x8_t (&f)[D / 16], const bf16
 // SPLIT: q and k also come as bf16 residuals (qk_lo [T, 2A], leading
 // dimension ldl); every score is q_hi.k_hi + q_hi.k_lo + q_lo.k_hi, which
 // keeps the scores at fp32-level accuracy.
+//
+// K, K_lo and V tiles are double-buffered in LDS: the loads of tile kt + 1
+// are issued right after the barrier that publishes tile kt, so they fly
+// while tile kt is multiplied.  The loop body is written out twice with the
+// two buffers swapped (the tile count is rounded up to even; the extra body
+// only joins the barrier) so that every LDS access names a fixed array.
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __restrict__ qkv,
                                                             int64_t ldq,
@@ -139,13 +158,12 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
                                                             int64_t ldl, bf16_t* __restrict__ out,
                                                             int64_t ldo, float* __restrict__ lse,
                                                             int S, int H, int W, float sl2) {
-  constexpr int KLD = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kBKV * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Ks_lo[SPLIT ? kBKV * KLD : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * kTLD];
+  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8;
+  __shared__ __attribute__((aligned(16))) bf16_t K0[TE], K1[TE], V0[TE], V1[TE];
+  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL];
   const int h = blockIdx.y, b = blockIdx.z;
   const int A = H * D;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q0 = blockIdx.x * kBQ;
   const int qw = q0 + wave * 32;
   const int qi = qw + (lane & 31);
@@ -154,6 +172,20 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   const bf16_t* Kp = base + A + h * D;
   const bf16_t* Vp = base + 2 * A + h * D;
   const bf16_t* lo_base = SPLIT ? qk_lo + (int64_t)b * S * ldl : nullptr;
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(Kp, ldq, S, D), rv = rows_rsrc(Vp, ldq, S, D);
+  const __amdgpu_buffer_rsrc_t rl =
+      SPLIT ? rows_rsrc(lo_base + A + h * D, ldl, S, D) : rk;
+  DmaRows<D> dma;
+  dma.init(wave, lane);
+
+  const int qlast = min(q0 + kBQ, S) - 1;
+  const int kt_lo = max(0, q0 - W + 1) / kBKV, kt_hi = qlast / kBKV;
+  auto issue = [&](bf16_t* k, bf16_t* kl, bf16_t* v, int kt) {
+    dma.issue(rk, k, wave, kt * kBKV, S, ldq);
+    if (SPLIT) dma.issue(rl, kl, wave, kt * kBKV, S, ldl);
+    dma.issue(rv, v, wave, kt * kBKV, S, ldq);
+  };
+  issue(K0, L0, V0, kt_lo);
 
   bf16x8_t qf[D / 16], qf_lo[D / 16];
   load_row_frags<D>(qf, Qp, ldq, qi, S, lane);
@@ -164,30 +196,14 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-
-  const int qlast = min(q0 + kBQ, S) - 1;
-  const int kt_lo = max(0, q0 - W + 1) / kBKV, kt_hi = qlast / kBKV;
   const bool wave_live = qw < S;
-  // tile kt + 1 is loaded into registers while tile kt is multiplied
-  RowTile<D> kreg, klreg;
-  RowTileT<D> vreg;
-  const bf16_t* Klp = SPLIT ? lo_base + A + h * D : nullptr;
-  kreg.load(Kp, ldq, kt_lo * kBKV, S);
-  if (SPLIT) klreg.load(Klp, ldl, kt_lo * kBKV, S);
-  vreg.load(Vp, ldq, kt_lo * kBKV, S);
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+
+  auto body = [&](const bf16_t* Ks, const bf16_t* Ks_lo, const bf16_t* Vs, bf16_t* nk,
+                  bf16_t* nl, bf16_t* nv, int kt) {
+    drain_barrier();
+    if (kt < kt_hi) issue(nk, nl, nv, kt + 1);
     const int j0 = kt * kBKV;
-    __syncthreads();
-    kreg.store(Ks);
-    if (SPLIT) klreg.store(Ks_lo);
-    vreg.store(Vt);
-    __syncthreads();
-    if (kt < kt_hi) {
-      kreg.load(Kp, ldq, j0 + kBKV, S);
-      if (SPLIT) klreg.load(Klp, ldl, j0 + kBKV, S);
-      vreg.load(Vp, ldq, j0 + kBKV, S);
-    }
-    if (!wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) continue;
+    if (kt > kt_hi || !wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) return;
     const bool full = (j0 + kBKV - 1 <= qw) && (qw + 31 - j0 < W) && (j0 + kBKV <= S);
     f32x16_t st[2];
 #pragma unroll
@@ -242,11 +258,13 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
       for (int hf = 0; hf < 2; ++hf) {
         const bf16x8_t pb = pack8(&p[kh][hf * 8]);
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) {
-          const bf16_t* vr = Vt + (mb * 32 + (lane & 31)) * kTLD + kh * 32 + hf * 16;
-          o[mb] = mfma32(ld_frag_reordered(vr, lane), pb, o[mb]);
-        }
+        for (int mb = 0; mb < D / 32; ++mb)
+          o[mb] = mfma32(ld_frag_tr<KLD>(Vs, kh * 32 + hf * 16, mb * 32, lane), pb, o[mb]);
       }
+  };
+  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+    body(K0, L0, V0, K1, L1, V1, kt);
+    body(K1, L1, V1, K0, L0, V0, kt + 1);
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qi < S) {
@@ -294,23 +312,23 @@ __global__ __launch_bounds__(256) void swa_rowdot(const T* __restrict__ d_o, int
 }
 
 // ------------------------------------------------------------------ dK, dV
+// Q, Q_lo and dO tiles double-buffered in LDS as in the forward; the
+// log-sum-exp and D values of the next query tile ride in registers of the
+// first wave and are written to LDS just before the barrier that publishes
+// their tile.
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
     const bf16_t* __restrict__ qkv, int64_t ldq, const bf16_t* __restrict__ qk_lo, int64_t ldl,
     const bf16_t* __restrict__ d_o, int64_t ld_do,
     const float* __restrict__ lse, const float* __restrict__ dvec, bf16_t* __restrict__ dqkv,
     int64_t ldd, int S, int H, int W, float sl2, float scale) {
-  constexpr int KLD = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[kBKV * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Qs_lo[SPLIT ? kBKV * KLD : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t dOs[kBKV * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[D * kTLD];
-  __shared__ __attribute__((aligned(16))) bf16_t dOt[D * kTLD];
-  __shared__ __attribute__((aligned(16))) float lse_s[kBKV];
-  __shared__ __attribute__((aligned(16))) float dv_s[kBKV];
+  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8;
+  __shared__ __attribute__((aligned(16))) bf16_t Q0[TE], Q1[TE], O0[TE], O1[TE];
+  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL];
+  __shared__ __attribute__((aligned(16))) float ls0[kBKV], ls1[kBKV], dd0[kBKV], dd1[kBKV];
   const int h = blockIdx.y, b = blockIdx.z;
   const int A = H * D;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int k0 = blockIdx.x * kBQ;
   const int kw = k0 + wave * 32;
   const int kj = kw + (lane & 31);
@@ -322,6 +340,26 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
   const float* lse_b = lse + ((int64_t)b * H + h) * S;
   const float* dv_b = dvec + ((int64_t)b * H + h) * S;
   const bf16_t* lo_base = SPLIT ? qk_lo + (int64_t)b * S * ldl : nullptr;
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(Qp, ldq, S, D), ro = rows_rsrc(dOp, ld_do, S, D);
+  const __amdgpu_buffer_rsrc_t rl = SPLIT ? rows_rsrc(lo_base + h * D, ldl, S, D) : rq;
+  DmaRows<D> dma;
+  dma.init(wave, lane);
+
+  const int klast = min(k0 + kBQ, S) - 1;
+  const int qt_lo = k0 / kBKV, qt_hi = min(S - 1, klast + W - 1) / kBKV;
+  float nls = 0.f, ndd = 0.f;  // next tile's lse and D, threads 0..63
+  auto issue = [&](bf16_t* q, bf16_t* ql, bf16_t* o, int qt) {
+    const int i0 = qt * kBKV;
+    dma.issue(rq, q, wave, i0, S, ldq);
+    if (SPLIT) dma.issue(rl, ql, wave, i0, S, ldl);
+    dma.issue(ro, o, wave, i0, S, ld_do);
+    if (threadIdx.x < kBKV) {
+      const int i = i0 + threadIdx.x;
+      nls = i < S ? lse_b[i] : 0.f;
+      ndd = i < S ? dv_b[i] : 0.f;
+    }
+  };
+  issue(Q0, L0, O0, qt_lo);
 
   bf16x8_t kf[D / 16], vf[D / 16], kf_lo[D / 16];
   load_row_frags<D>(kf, Kp, ldq, kj, S, lane);
@@ -332,27 +370,15 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dk[mb][r] = 0.f; dv[mb][r] = 0.f; }
-
-  const int klast = min(k0 + kBQ, S) - 1;
-  const int qt_lo = k0 / kBKV, qt_hi = min(S - 1, klast + W - 1) / kBKV;
   const bool wave_live = kw < S;
-  for (int qt = qt_lo; qt <= qt_hi; ++qt) {
+
+  auto body = [&](const bf16_t* Qs, const bf16_t* Qs_lo, const bf16_t* dOs, float* lse_s,
+                  float* dv_s, bf16_t* nq, bf16_t* nql, bf16_t* no, int qt) {
+    if (threadIdx.x < kBKV) { lse_s[threadIdx.x] = nls * kLog2e; dv_s[threadIdx.x] = ndd; }
+    drain_barrier();
+    if (qt < qt_hi) issue(nq, nql, no, qt + 1);
     const int i0 = qt * kBKV;
-    __syncthreads();
-    // each array's loads in flight at once, then its LDS stores (one array
-    // at a time: this kernel holds dK and dV for 128 keys in registers)
-    stage<RowTile<D>>(Qs, Qp, ldq, i0, S);
-    if (SPLIT) stage<RowTile<D>>(Qs_lo, lo_base + h * D, ldl, i0, S);
-    stage<RowTile<D>>(dOs, dOp, ld_do, i0, S);
-    stage<RowTileT<D>>(Qt, Qp, ldq, i0, S);
-    stage<RowTileT<D>>(dOt, dOp, ld_do, i0, S);
-    if (threadIdx.x < kBKV) {
-      const int i = i0 + threadIdx.x;
-      lse_s[threadIdx.x] = i < S ? lse_b[i] * kLog2e : 0.f;
-      dv_s[threadIdx.x] = i < S ? dv_b[i] : 0.f;
-    }
-    __syncthreads();
-    if (!wave_live || i0 > kw + 31 + W - 1 || i0 + kBKV - 1 < kw) continue;
+    if (qt > qt_hi || !wave_live || i0 > kw + 31 + W - 1 || i0 + kBKV - 1 < kw) return;
     const bool full = (i0 >= kw + 31) && (i0 + kBKV - 1 - kw < W) && (i0 + kBKV <= S);
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
@@ -395,12 +421,15 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
         const bf16x8_t db = pack8(&ds[hf * 8]);
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) {
-          const int ro = (mb * 32 + (lane & 31)) * kTLD + qh * 32 + hf * 16;
-          dv[mb] = mfma32(ld_frag_reordered(dOt + ro, lane), pb, dv[mb]);
-          dk[mb] = mfma32(ld_frag_reordered(Qt + ro, lane), db, dk[mb]);
+          dv[mb] = mfma32(ld_frag_tr<KLD>(dOs, qh * 32 + hf * 16, mb * 32, lane), pb, dv[mb]);
+          dk[mb] = mfma32(ld_frag_tr<KLD>(Qs, qh * 32 + hf * 16, mb * 32, lane), db, dk[mb]);
         }
       }
     }
+  };
+  for (int qt = qt_lo; qt <= qt_hi; qt += 2) {
+    body(Q0, L0, O0, ls0, dd0, Q1, L1, O1, qt);
+    body(Q1, L1, O1, ls1, dd1, Q0, L0, O0, qt + 1);
   }
   if (kj < S) {
     bf16_t* row = dqkv + ((int64_t)b * S + kj) * ldd + h * D;
@@ -421,20 +450,19 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
 }
 
 // ------------------------------------------------------------------ dQ
+// K, K_lo and V tiles double-buffered in LDS as in the forward.
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
     const bf16_t* __restrict__ qkv, int64_t ldq, const bf16_t* __restrict__ qk_lo, int64_t ldl,
     const bf16_t* __restrict__ d_o, int64_t ld_do,
     const float* __restrict__ lse, const float* __restrict__ dvec, bf16_t* __restrict__ dqkv,
     int64_t ldd, int S, int H, int W, float sl2, float scale) {
-  constexpr int KLD = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kBKV * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Ks_lo[SPLIT ? kBKV * KLD : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[kBKV * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[D * kTLD];
+  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8;
+  __shared__ __attribute__((aligned(16))) bf16_t K0[TE], K1[TE], V0[TE], V1[TE];
+  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL];
   const int h = blockIdx.y, b = blockIdx.z;
   const int A = H * D;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q0 = blockIdx.x * kBQ;
   const int qw = q0 + wave * 32;
   const int qi = qw + (lane & 31);
@@ -444,6 +472,20 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   const bf16_t* Vp = base + 2 * A + h * D;
   const bf16_t* dOp = d_o + (int64_t)b * S * ld_do + h * D;
   const bf16_t* lo_base = SPLIT ? qk_lo + (int64_t)b * S * ldl : nullptr;
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(Kp, ldq, S, D), rv = rows_rsrc(Vp, ldq, S, D);
+  const __amdgpu_buffer_rsrc_t rl =
+      SPLIT ? rows_rsrc(lo_base + A + h * D, ldl, S, D) : rk;
+  DmaRows<D> dma;
+  dma.init(wave, lane);
+
+  const int qlast = min(q0 + kBQ, S) - 1;
+  const int kt_lo = max(0, q0 - W + 1) / kBKV, kt_hi = qlast / kBKV;
+  auto issue = [&](bf16_t* k, bf16_t* kl, bf16_t* v, int kt) {
+    dma.issue(rk, k, wave, kt * kBKV, S, ldq);
+    if (SPLIT) dma.issue(rl, kl, wave, kt * kBKV, S, ldl);
+    dma.issue(rv, v, wave, kt * kBKV, S, ldq);
+  };
+  issue(K0, L0, V0, kt_lo);
 
   bf16x8_t qf[D / 16], of[D / 16], qf_lo[D / 16];
   load_row_frags<D>(qf, Qp, ldq, qi, S, lane);
@@ -456,27 +498,14 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[mb][r] = 0.f;
-
-  const int qlast = min(q0 + kBQ, S) - 1;
-  const int kt_lo = max(0, q0 - W + 1) / kBKV, kt_hi = qlast / kBKV;
   const bool wave_live = qw < S;
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+
+  auto body = [&](const bf16_t* Ks, const bf16_t* Ks_lo, const bf16_t* Vs, bf16_t* nk,
+                  bf16_t* nl, bf16_t* nv, int kt) {
+    drain_barrier();
+    if (kt < kt_hi) issue(nk, nl, nv, kt + 1);
     const int j0 = kt * kBKV;
-    __syncthreads();
-    {  // every load of the tile in flight at once, then the LDS stores
-      RowTile<D> k, kl, v;
-      RowTileT<D> kt_;
-      k.load(Kp, ldq, j0, S);
-      if (SPLIT) kl.load(lo_base + A + h * D, ldl, j0, S);
-      v.load(Vp, ldq, j0, S);
-      kt_.load(Kp, ldq, j0, S);
-      k.store(Ks);
-      if (SPLIT) kl.store(Ks_lo);
-      v.store(Vs);
-      kt_.store(Kt);
-    }
-    __syncthreads();
-    if (!wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) continue;
+    if (kt > kt_hi || !wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) return;
     const bool full = (j0 + kBKV - 1 <= qw) && (qw + 31 - j0 < W) && (j0 + kBKV <= S);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -508,12 +537,14 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
       for (int hf = 0; hf < 2; ++hf) {
         const bf16x8_t db = pack8(&ds[hf * 8]);
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) {
-          const bf16_t* kr = Kt + (mb * 32 + (lane & 31)) * kTLD + kh * 32 + hf * 16;
-          dq[mb] = mfma32(ld_frag_reordered(kr, lane), db, dq[mb]);
-        }
+        for (int mb = 0; mb < D / 32; ++mb)
+          dq[mb] = mfma32(ld_frag_tr<KLD>(Ks, kh * 32 + hf * 16, mb * 32, lane), db, dq[mb]);
       }
     }
+  };
+  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+    body(K0, L0, V0, K1, L1, V1, kt);
+    body(K1, L1, V1, K0, L0, V0, kt + 1);
   }
   if (qi < S) {
     bf16_t* row = dqkv + ((int64_t)b * S + qi) * ldd + h * D;
