@@ -124,6 +124,39 @@ def time_serial(cfg, inputs, args, ptb_ms):
             "ptb_speedup": round((f + b) / ptb_ms, 4)}
 
 
+def time_lamb_shard(params, args, dp=8):
+    """One data-parallel rank's half-steps of ZeRO-2 sharded LAMB (rank 0 of
+    `dp`, its 1/dp range of every tensor): lamb_shard_norms then
+    lamb_shard_apply.  The all-reduce of the 12 norms between them is a
+    collective across ranks and is not part of the timed kernels."""
+    import numpy as np
+    import torch
+    from transformer_block_lamb_amd.device import ShardedLamb
+    from transformer_block_lamb_amd.synth import LAMB_HPARAMS
+    hp = LAMB_HPARAMS
+    sh = ShardedLamb(params, dp)
+    mine = sh.ranks[0]["params"]
+
+    def half_steps(it):
+        n = sh.norms(0, it, hp["beta1"], hp["beta2"], hp["eps"])
+        sh.apply(0, n, it, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"])
+
+    for it in range(1, args.warmup + 1):
+        half_steps(it)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record()
+        half_steps(args.warmup + 1 + k)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    nb = lamb_bytes(mine)
+    return {"dp": dp, "rank_params": int(sum(p["w"].numel() for p in mine)),
+            "ms": round(ms, 4), "gbps": round(nb / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nb / (ms * 1e-3) / PEAK_HBM, 4)}
+
+
 def cpu_baseline(cfg, inputs, model_flops):
     """The fp64 oracle's forward + backward of one full step of the workload."""
     from oracle import ptb as O
@@ -243,6 +276,7 @@ def main():
     serial = None
     if not args.no_serial:
         serial = time_serial(cfg, inputs, args, fwd_ms + bwd_ms)
+    lamb_shard = time_lamb_shard(params, args)
 
     flops = stage_flops(cfg)
     n_mat = (3 * A + F) * cfg.hidden + (A + F) * cfg.hidden
@@ -274,7 +308,8 @@ def main():
         "fwd_bwd_ms_min": round(float(np.min(fb_each)), 4),
         "lamb_gbps": round(lb / (lamb_ms * 1e-3) / 1e9, 1),
         "lamb_hbm_frac": round(lb / (lamb_ms * 1e-3) / PEAK_HBM, 4),
-        "lamb_bytes": lb, "executed_tflops": round(executed, 2),
+        "lamb_bytes": lb, "lamb_zero2_rank": lamb_shard,
+        "executed_tflops": round(executed, 2),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4),
         "stages_ms": {n: round(v, 4) for n, v in per_stage.items()},
         "roofline": roofline,

@@ -167,6 +167,34 @@ int lamb_step(const lamb_tensor* tensors, int32_t n_tensors, float lr, float bet
               float eps, int64_t step, float* ratios_out, void* scratch, size_t scratch_bytes,
               hipStream_t stream);
 
+/* Sharded LAMB for data-parallel training with ZeRO-2 optimizer sharding
+ * (MegaScale study guide, ch.2 §2.1 parallelism table, DP (+ZeRO-2) row:
+ * optimizer state and gradients are split over the data-parallel ranks;
+ * the trust ratio as in lamb_step): every rank owns a contiguous element range of each
+ * tensor, and the descriptors passed here point at this rank's range (n =
+ * its length; any split works, the step is elementwise apart from the two
+ * norms).  The step splits at the norms:
+ *   lamb_shard_norms  updates m and v of the shard in place exactly as
+ *                     lamb_step does and writes norms_out[2 t] = sum of w^2
+ *                     and norms_out[2 t + 1] = sum of u^2 over the shard
+ *                     (device fp64 [2 n_tensors], 8-byte aligned);
+ *   (caller)          sums norms_out over the ranks, e.g. an all-reduce of
+ *                     2 n_tensors doubles, into `norms`;
+ *   lamb_shard_apply  r_t = sqrt(norms[2t]) / sqrt(norms[2t+1]) (1 if either
+ *                     is 0), then w <- w - lr * r_t * u on the shard (and
+ *                     w_bf16 if given); g may be NULL here.
+ * With one shard per tensor this is lamb_step; across shards the results
+ * differ from it only by the order of the fp64 norm sums.  Same scratch
+ * size and rules as lamb_step (lamb_scratch_bytes of the shard
+ * descriptors); the two halves must see the same hyper-parameters and
+ * step.  Errors as lamb_step. */
+int lamb_shard_norms(const lamb_tensor* tensors, int32_t n_tensors, float beta1, float beta2,
+                     float eps, int64_t step, double* norms_out, void* scratch,
+                     size_t scratch_bytes, hipStream_t stream);
+int lamb_shard_apply(const lamb_tensor* tensors, int32_t n_tensors, float lr, float beta1,
+                     float beta2, float eps, int64_t step, const double* norms,
+                     float* ratios_out, void* scratch, size_t scratch_bytes, hipStream_t stream);
+
 /* Human-readable text of a status code (static string). */
 const char* ptb_status_string(int status);
 

@@ -51,3 +51,41 @@ def lamb_step(tensors, step, lr, beta1, beta2, eps, weight_decay):
                                          lr, beta1, beta2, eps, wd)
         out.append(dict(w=w, m=m, v=v, ratio=r))
     return out
+
+
+# ZeRO-2 sharding (MegaScale study guide, ch.2 §2.1 parallelism table,
+# DP (+ZeRO-2) row: optimizer state and gradients are split over the
+# data-parallel ranks).  Each rank holds a contiguous slice of every tensor.
+# The step above is elementwise except for the two norms, and a squared
+# norm is a sum over elements, so the sharded step is: every rank updates
+# its slice of m and v and sums w^2 and u^2 over its slice; the ranks add
+# those sums (an all-reduce); every rank forms the same ratio from the
+# totals and updates its slice of w.
+
+def lamb_shard_norms(w, g, m, v, step, beta1, beta2, eps, weight_decay):
+    """First half on one rank's slice.  Returns (m_new, v_new, sum w^2, sum u^2)."""
+    w = np.asarray(w, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m_new = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v_new = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * g * g
+    u = _update(w, m_new, v_new, step, beta1, beta2, eps, weight_decay)
+    return m_new, v_new, float(np.sum(w * w)), float(np.sum(u * u))
+
+
+def lamb_shard_apply(w, m_new, v_new, w_sq_total, u_sq_total, step, lr, beta1, beta2, eps,
+                     weight_decay):
+    """Second half on one rank's slice, from the norms summed over all ranks.
+    Returns (w_new, ratio)."""
+    w = np.asarray(w, dtype=np.float64)
+    u = _update(w, np.asarray(m_new, dtype=np.float64), np.asarray(v_new, dtype=np.float64),
+                step, beta1, beta2, eps, weight_decay)
+    ratio = (np.sqrt(w_sq_total) / np.sqrt(u_sq_total)
+             if (w_sq_total > 0.0 and u_sq_total > 0.0) else 1.0)
+    return w - lr * ratio * u, float(ratio)
+
+
+def _update(w, m_new, v_new, step, beta1, beta2, eps, weight_decay):
+    """u of the published method from the updated moments."""
+    m_hat = m_new / (1.0 - beta1 ** step)
+    v_hat = v_new / (1.0 - beta2 ** step)
+    return m_hat / (np.sqrt(v_hat) + eps) + weight_decay * w

@@ -94,6 +94,22 @@ def test_lamb_argument_checks():
     for bad in (T(100, gdt=5), T(100, w=fake + 4), T(0), T(100, wc=fake + 2)):
         one = (B.LambTensor * 1)(bad)
         assert L.lamb_step(one, 1, 1e-3, 0.9, 0.999, 1e-6, 1, None, fake, need, None) == -1
+    # the sharded halves: same checks, plus the fp64 norms buffer
+    assert L.lamb_shard_norms(arr, 2, 0.9, 0.999, 1e-6, 1, None, fake, need, None) == -1
+    assert L.lamb_shard_norms(arr, 2, 0.9, 0.999, 1e-6, 1, fake + 4, fake, need, None) == -1
+    assert L.lamb_shard_norms(arr, 2, 0.9, 0.999, 1e-6, 0, fake, fake, need, None) == -1
+    assert L.lamb_shard_norms(arr, 2, 0.9, 0.999, 1e-6, 1, fake, fake, need - 1, None) == -3
+    assert L.lamb_shard_apply(arr, 2, 1e-3, 0.9, 0.999, 1e-6, 1, None, None, fake, need,
+                              None) == -1
+    assert L.lamb_shard_apply(arr, 2, 1e-3, 0.9, 0.999, 1e-6, 1, fake, fake + 2, fake, need,
+                              None) == -1
+    assert L.lamb_shard_apply(arr, 2, float("nan"), 0.9, 0.999, 1e-6, 1, fake, None, fake, need,
+                              None) == -1
+    for bad in (T(100, gdt=5), T(100, w=fake + 4), T(0)):
+        one = (B.LambTensor * 1)(bad)
+        assert L.lamb_shard_norms(one, 1, 0.9, 0.999, 1e-6, 1, fake, fake, need, None) == -1
+        assert L.lamb_shard_apply(one, 1, 1e-3, 0.9, 0.999, 1e-6, 1, fake, None, fake, need,
+                                  None) == -1
 
 
 def test_component_argument_checks():

@@ -1,14 +1,16 @@
 """Parity of lamb_step (through the C ABI) against the fp64 oracle: updated
 weights compared as the update dw = w' - w, moments m and v, per-tensor
 trust ratios; the norm invariant ||w' - w|| = lr ||w||; resume from saved
-state; the full 175B TP=8 layer shard (226.5M parameters)."""
+state; the full 175B TP=8 layer shard (226.5M parameters); the ZeRO-2
+sharded halves (lamb_shard_norms / lamb_shard_apply) against lamb_step and
+the oracle."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import lamb as OL
 from parity import check, half_ulp
-from transformer_block_lamb_amd.device import LambState
+from transformer_block_lamb_amd.device import LambState, ShardedLamb
 from transformer_block_lamb_amd.synth import LAMB_175B_TENSORS, LAMB_HPARAMS, lamb_grads, lamb_inputs
 
 pytestmark = pytest.mark.gpu
@@ -33,14 +35,15 @@ def _oracle_steps(tensors, grads_per_step, first_step):
     return state, ratios
 
 
-def _compare(dev, w0, ref_state, ref_ratios, tol_dtype="f32"):
+def _compare(dev, w0, ref_state, ref_ratios, tol_dtype="f32", ratios=None):
     for i, (p, ref) in enumerate(zip(dev.params, ref_state)):
         # the update w' - w, allowing for the rounding of w' to fp32
         check(f"dw[{i}]", _host(p["w"]) - w0[i], ref["w"] - w0[i], tol_dtype,
               allowance=2 * half_ulp(ref["w"], "f32"))
         check(f"m[{i}]", _host(p["m"]), ref["m"], tol_dtype)
         check(f"v[{i}]", _host(p["v"]), ref["v"], tol_dtype)
-    np.testing.assert_allclose(_host(dev.ratios), ref_ratios, rtol=1e-4)
+    np.testing.assert_allclose(_host(dev.ratios if ratios is None else ratios), ref_ratios,
+                               rtol=1e-4)
 
 
 @pytest.mark.parametrize("grad_dtype", ["bf16", "f32"])
@@ -137,3 +140,48 @@ def test_lamb_full_175b_shard():
     torch.cuda.synchronize()
     ref, ratios = _oracle_steps(ts, [[t["g"] for t in ts]], 1)
     _compare(dev, w0, ref, ratios)
+
+
+def _sharded_vs_full(sizes, n_shards, steps, oracle=False):
+    ts = lamb_inputs(sizes)
+    full = LambState(ts, "bf16", bf16_copy=True)
+    sharded_state = LambState(ts, "bf16", bf16_copy=True)
+    sh = ShardedLamb(sharded_state.params, n_shards)
+    w0 = [t["w"].astype(np.float64) for t in ts]
+    for s in range(1, steps + 1):
+        if s > 1:
+            g = lamb_grads(sizes, s)
+            full.set_grads(g)
+            sharded_state.set_grads(g)
+        full.step(s, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"])
+        sh.step(s, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"])
+    torch.cuda.synchronize()
+    for i, (pa, pb) in enumerate(zip(full.params, sharded_state.params)):
+        # pass A is elementwise: the moments match bit for bit
+        assert torch.equal(pa["m"], pb["m"]), i
+        assert torch.equal(pa["v"], pb["v"]), i
+        # the norms are added in another order (fp64), which can move the
+        # ratio by an fp32 ulp: w within 3 ulps of the larger of the old and
+        # new magnitudes (w - lr r u can cancel to far below either)
+        a, b = _host(pa["w"]), _host(pb["w"])
+        mag = np.maximum(np.abs(a), np.abs(w0[i])).astype(np.float32)
+        assert np.all(np.abs(a - b) <= 3 * np.spacing(mag)), i
+        assert torch.equal(pb["w_bf16"], pb["w"].to(torch.bfloat16)), i
+    np.testing.assert_allclose(_host(sh.ratios), _host(full.ratios), rtol=1e-6)
+    if oracle:
+        ref, ratios = _oracle_steps(ts, [[t["g"] for t in ts]], 1)
+        _compare(sharded_state, w0, ref, ratios, ratios=sh.ratios)
+
+
+@pytest.mark.parametrize("n_shards", [2, 3, 8])
+def test_lamb_sharded_equals_unsharded(n_shards):
+    """Ragged ranges; the smallest tensors do not reach every rank."""
+    print(f"lamb sharded x{n_shards}", flush=True)
+    _sharded_vs_full(SMALL, n_shards, 1, oracle=True)
+    _sharded_vs_full(SMALL, n_shards, 3)
+
+
+def test_lamb_sharded_175b_dp8():
+    sizes = [n for _, n in LAMB_175B_TENSORS]
+    print(f"lamb sharded 175B x8 {sum(sizes)} params", flush=True)
+    _sharded_vs_full(sizes, 8, 1)

@@ -23,7 +23,7 @@ EXPORTED = ("ptb_saved_bytes", "ptb_scratch_bytes", "ptb_forward", "ptb_backward
             "ptb_forward_stage", "ptb_backward_stage",
             "ptb_layernorm_forward", "ptb_gemm_workspace_bytes", "ptb_gemm", "ptb_swa_forward",
             "ptb_swa_backward", "ptb_serial_saved_bytes", "ptb_serial_scratch_bytes",
-            "ptb_serial_forward", "ptb_serial_backward")
+            "ptb_serial_forward", "ptb_serial_backward", "lamb_shard_norms", "lamb_shard_apply")
 FWD_STAGES = ("layernorm", "gemm_in", "attention", "gemm_out")
 BWD_STAGES = ("gemm_dcat", "gemm_dw_out", "attention", "gemm_dw_in", "gemm_dxn", "layernorm")
 
@@ -73,6 +73,9 @@ def lib():
                                                   vp, vp, vp, sz, vp]),
             "lamb_scratch_bytes": (sz, [pl, i32]),
             "lamb_step": (ctypes.c_int, [pl, i32, f32, f32, f32, f32, i64, vp, vp, sz, vp]),
+            "lamb_shard_norms": (ctypes.c_int, [pl, i32, f32, f32, f32, i64, vp, vp, sz, vp]),
+            "lamb_shard_apply": (ctypes.c_int, [pl, i32, f32, f32, f32, f32, i64, vp, vp, vp, sz,
+                                                vp]),
             "ptb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "ptb_layernorm_forward": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp,
                                                      vp]),
@@ -198,6 +201,24 @@ def lamb_step(tensors, lr, beta1, beta2, eps, step, ratios_out, scratch, stream=
                            _ptr(ratios_out), _ptr(scratch),
                            scratch.numel() * scratch.element_size(), _stream(stream)),
            "lamb_step")
+
+
+def lamb_shard_norms(tensors, beta1, beta2, eps, step, norms_out, scratch, stream=None):
+    """First half of the sharded step: m, v of the shard updated; norms_out
+    (fp64 [2 n]) receives the shard's sums of w^2 and u^2 per tensor."""
+    _check(lib().lamb_shard_norms(tensors, len(tensors), beta1, beta2, eps, step,
+                                  _ptr(norms_out), _ptr(scratch),
+                                  scratch.numel() * scratch.element_size(), _stream(stream)),
+           "lamb_shard_norms")
+
+
+def lamb_shard_apply(tensors, lr, beta1, beta2, eps, step, norms, ratios_out, scratch,
+                     stream=None):
+    """Second half: w of the shard updated from the norms summed over shards."""
+    _check(lib().lamb_shard_apply(tensors, len(tensors), lr, beta1, beta2, eps, step,
+                                  _ptr(norms), _ptr(ratios_out), _ptr(scratch),
+                                  scratch.numel() * scratch.element_size(), _stream(stream)),
+           "lamb_shard_apply")
 
 
 def ptb_status_string(status: int) -> str:

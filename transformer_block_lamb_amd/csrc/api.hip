@@ -523,19 +523,24 @@ size_t lamb_scratch_bytes(const lamb_tensor* t, int32_t n) {
   return up((size_t)blocks * 2 * sizeof(float)) + up((size_t)n * sizeof(float));
 }
 
-int lamb_step(const lamb_tensor* t, int32_t n, float lr, float beta1, float beta2, float eps,
-              int64_t step, float* ratios_out, void* scratch, size_t scratch_bytes,
-              hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks a LAMB call (the gradient may be absent only when `need_grad` is
+// false) and fills the hyper-parameters and the total block count.
+int lamb_check(const lamb_tensor* t, int32_t n, float lr, float beta1, float beta2, float eps,
+               int64_t step, void* scratch, size_t scratch_bytes, bool need_grad, LambHyper& hp,
+               int64_t& total_blocks) {
   if (t == nullptr || n < 1 || step < 1) return PTB_ERR_INVALID_ARG;
   if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f &&
         isfinite(lr)))
     return PTB_ERR_INVALID_ARG;
   if (scratch == nullptr || !aligned16(scratch)) return PTB_ERR_INVALID_ARG;
-  if (ratios_out != nullptr && (reinterpret_cast<uintptr_t>(ratios_out) & 3u))
-    return PTB_ERR_INVALID_ARG;
-  int64_t total_blocks = 0;
+  total_blocks = 0;
   for (int i = 0; i < n; ++i) {
-    if (t[i].n < 1 || !all_aligned({t[i].w, t[i].g, t[i].m, t[i].v})) return PTB_ERR_INVALID_ARG;
+    if (t[i].n < 1 || !all_aligned({t[i].w, t[i].m, t[i].v})) return PTB_ERR_INVALID_ARG;
+    if ((need_grad || t[i].g != nullptr) && !all_aligned({t[i].g})) return PTB_ERR_INVALID_ARG;
     if (t[i].w_bf16 != nullptr && !aligned16(t[i].w_bf16)) return PTB_ERR_INVALID_ARG;
     if (t[i].grad_dtype != PTB_F32 && t[i].grad_dtype != PTB_BF16) return PTB_ERR_INVALID_ARG;
     if (!isfinite(t[i].weight_decay)) return PTB_ERR_INVALID_ARG;
@@ -543,15 +548,17 @@ int lamb_step(const lamb_tensor* t, int32_t n, float lr, float beta1, float beta
   }
   if (total_blocks > INT32_MAX / 2) return PTB_ERR_UNSUPPORTED;
   if (scratch_bytes < lamb_scratch_bytes(t, n)) return PTB_ERR_WORKSPACE;
-  float* partials = static_cast<float*>(scratch);
-  float* ratios = at<float>(scratch, up((size_t)total_blocks * 2 * sizeof(float)));
-
-  LambHyper hp;
   hp.lr = lr; hp.beta1 = beta1; hp.beta2 = beta2; hp.eps = eps;
   hp.bc1 = (float)(1.0 - pow((double)beta1, (double)step));
   hp.bc2 = (float)(1.0 - pow((double)beta2, (double)step));
   if (!(hp.bc1 > 0.f && hp.bc2 > 0.f)) return PTB_ERR_INVALID_ARG;
+  return PTB_OK;
+}
 
+// Runs `launch(batch, first tensor, first block)` over the tensors in
+// groups of at most kLambMaxTensors (one kernel-argument table each).
+template <class F>
+int lamb_batches(const lamb_tensor* t, int32_t n, F&& launch) {
   int64_t blk_off = 0;
   for (int first = 0; first < n; first += kLambMaxTensors) {
     LambBatch b;
@@ -566,12 +573,66 @@ int lamb_step(const lamb_tensor* t, int32_t n, float lr, float beta1, float beta
       blk += (int)lamb_blocks_for(ti.n);
     }
     b.blk_start[b.ntensors] = blk;
-    hipError_t e = launch_lamb(b, hp, partials + 2 * blk_off, ratios + first,
-                               ratios_out ? ratios_out + first : nullptr, stream);
-    if (e != hipSuccess) return PTB_ERR_HIP;
+    if (launch(b, first, blk_off) != hipSuccess) return PTB_ERR_HIP;
     blk_off += blk;
   }
   return PTB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lamb_step(const lamb_tensor* t, int32_t n, float lr, float beta1, float beta2, float eps,
+              int64_t step, float* ratios_out, void* scratch, size_t scratch_bytes,
+              hipStream_t stream) {
+  LambHyper hp;
+  int64_t total_blocks;
+  const int st =
+      lamb_check(t, n, lr, beta1, beta2, eps, step, scratch, scratch_bytes, true, hp, total_blocks);
+  if (st != PTB_OK) return st;
+  if (ratios_out != nullptr && (reinterpret_cast<uintptr_t>(ratios_out) & 3u))
+    return PTB_ERR_INVALID_ARG;
+  float* partials = static_cast<float*>(scratch);
+  float* ratios = at<float>(scratch, up((size_t)total_blocks * 2 * sizeof(float)));
+  return lamb_batches(t, n, [&](const LambBatch& b, int first, int64_t blk_off) {
+    return launch_lamb(b, hp, partials + 2 * blk_off, ratios + first,
+                       ratios_out ? ratios_out + first : nullptr, stream);
+  });
+}
+
+int lamb_shard_norms(const lamb_tensor* t, int32_t n, float beta1, float beta2, float eps,
+                     int64_t step, double* norms_out, void* scratch, size_t scratch_bytes,
+                     hipStream_t stream) {
+  LambHyper hp;
+  int64_t total_blocks;
+  const int st = lamb_check(t, n, 0.f, beta1, beta2, eps, step, scratch, scratch_bytes, true, hp,
+                            total_blocks);
+  if (st != PTB_OK) return st;
+  if (norms_out == nullptr || (reinterpret_cast<uintptr_t>(norms_out) & 7u))
+    return PTB_ERR_INVALID_ARG;
+  float* partials = static_cast<float*>(scratch);
+  return lamb_batches(t, n, [&](const LambBatch& b, int first, int64_t blk_off) {
+    return launch_lamb_norms(b, hp, partials + 2 * blk_off, norms_out + 2 * first, stream);
+  });
+}
+
+int lamb_shard_apply(const lamb_tensor* t, int32_t n, float lr, float beta1, float beta2,
+                     float eps, int64_t step, const double* norms, float* ratios_out,
+                     void* scratch, size_t scratch_bytes, hipStream_t stream) {
+  LambHyper hp;
+  int64_t total_blocks;
+  const int st = lamb_check(t, n, lr, beta1, beta2, eps, step, scratch, scratch_bytes, false, hp,
+                            total_blocks);
+  if (st != PTB_OK) return st;
+  if (norms == nullptr || (reinterpret_cast<uintptr_t>(norms) & 7u)) return PTB_ERR_INVALID_ARG;
+  if (ratios_out != nullptr && (reinterpret_cast<uintptr_t>(ratios_out) & 3u))
+    return PTB_ERR_INVALID_ARG;
+  float* ratios = at<float>(scratch, up((size_t)total_blocks * 2 * sizeof(float)));
+  return lamb_batches(t, n, [&](const LambBatch& b, int first, int64_t) {
+    return launch_lamb_apply(b, hp, norms + 2 * first, ratios + first,
+                             ratios_out ? ratios_out + first : nullptr, stream);
+  });
 }
 
 // ------------------------------------------------------------------ components

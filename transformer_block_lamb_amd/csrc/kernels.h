@@ -100,5 +100,9 @@ struct LambHyper {
 int64_t lamb_blocks_for(int64_t n);
 hipError_t launch_lamb(const LambBatch& b, const LambHyper& hp, float* partials, float* ratios,
                        float* ratios_out, hipStream_t s);
+hipError_t launch_lamb_norms(const LambBatch& b, const LambHyper& hp, float* partials,
+                             double* norms, hipStream_t s);
+hipError_t launch_lamb_apply(const LambBatch& b, const LambHyper& hp, const double* norms,
+                             float* ratios, float* ratios_out, hipStream_t s);
 
 }  // namespace ptb

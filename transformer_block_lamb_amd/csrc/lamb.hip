@@ -14,6 +14,12 @@
 //            pass A; writes w - lr * r * u                (16 bytes/param)
 //            and, when asked, a bf16 copy of the new w for the next
 //            forward                                      (+2 bytes/param)
+// The sharded form (ZeRO-2: each data-parallel rank owns a contiguous
+// element range of every tensor) splits the step at the norms: pass A plus
+// a finalize that stores the shard's fp64 sums of w^2 and u^2 per tensor;
+// the caller adds those over the ranks (an all-reduce of 2 doubles per
+// tensor); then the ratios come from the summed norms and pass B runs on
+// the shard.
 // All tensors of a call share one launch per pass (a kernel-argument table
 // of up to 16 tensors; a workgroup finds its tensor from the block ranges).
 // Each thread moves 16-byte vectors (4 fp32) and keeps 4 of them in flight
@@ -161,12 +167,9 @@ __global__ __launch_bounds__(kLambThreads) void lamb_pass_a(LambBatch b, LambHyp
 // One workgroup of 1024 threads per tensor; thread i adds partials i,
 // i + 1024, ... in fp64, then the 16 wave sums are added in wave order.
 constexpr int kFinThreads = 1024;
-__global__ __launch_bounds__(kFinThreads) void lamb_finalize(LambBatch b,
-                                                             const float* __restrict__ partials,
-                                                             float* __restrict__ ratios,
-                                                             float* __restrict__ ratios_out) {
+__device__ __forceinline__ void tensor_sums(const LambBatch& b, const float* __restrict__ partials,
+                                            int t, double& W, double& U) {
   __shared__ double red[2][kFinThreads / 64];
-  const int t = blockIdx.x;
   double sw = 0.0, su = 0.0;
 #pragma unroll 4
   for (int blk = b.blk_start[t] + threadIdx.x; blk < b.blk_start[t + 1]; blk += kFinThreads) {
@@ -182,13 +185,49 @@ __global__ __launch_bounds__(kFinThreads) void lamb_finalize(LambBatch b,
   const int wid = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { red[0][wid] = sw; red[1][wid] = su; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double W = 0.0, U = 0.0;
+  W = 0.0;
+  U = 0.0;
+  if (threadIdx.x == 0)
     for (int i = 0; i < kFinThreads / 64; ++i) { W += red[0][i]; U += red[1][i]; }
-    const float r = (W > 0.0 && U > 0.0) ? (float)(sqrt(W) / sqrt(U)) : 1.0f;
-    ratios[t] = r;
-    if (ratios_out != nullptr) ratios_out[t] = r;
+}
+
+__device__ __forceinline__ float trust_ratio(double W, double U) {
+  return (W > 0.0 && U > 0.0) ? (float)(sqrt(W) / sqrt(U)) : 1.0f;
+}
+
+__global__ __launch_bounds__(kFinThreads) void lamb_finalize(LambBatch b,
+                                                             const float* __restrict__ partials,
+                                                             float* __restrict__ ratios,
+                                                             float* __restrict__ ratios_out) {
+  double W, U;
+  tensor_sums(b, partials, blockIdx.x, W, U);
+  if (threadIdx.x == 0) {
+    const float r = trust_ratio(W, U);
+    ratios[blockIdx.x] = r;
+    if (ratios_out != nullptr) ratios_out[blockIdx.x] = r;
   }
+}
+
+// Sharded step, first half: this shard's sum of w^2 and u^2 per tensor.
+__global__ __launch_bounds__(kFinThreads) void lamb_finalize_norms(
+    LambBatch b, const float* __restrict__ partials, double* __restrict__ norms) {
+  double W, U;
+  tensor_sums(b, partials, blockIdx.x, W, U);
+  if (threadIdx.x == 0) {
+    norms[2 * blockIdx.x] = W;
+    norms[2 * blockIdx.x + 1] = U;
+  }
+}
+
+// Sharded step, second half: the ratios from the norms summed over shards.
+__global__ __launch_bounds__(64) void lamb_ratios_from_norms(int n, const double* __restrict__ norms,
+                                                             float* __restrict__ ratios,
+                                                             float* __restrict__ ratios_out) {
+  const int t = threadIdx.x;
+  if (t >= n) return;
+  const float r = trust_ratio(norms[2 * t], norms[2 * t + 1]);
+  ratios[t] = r;
+  if (ratios_out != nullptr) ratios_out[t] = r;
 }
 
 __global__ __launch_bounds__(kLambThreads) void lamb_pass_b(LambBatch b, LambHyper hp,
@@ -246,6 +285,29 @@ hipError_t launch_lamb(const LambBatch& b, const LambHyper& hp, float* partials,
                      (const float*)partials, ratios, ratios_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lamb_pass_b, dim3(nblk), dim3(kLambThreads), 0, s, b, hp,
+                     (const float*)ratios);
+  return hipGetLastError();
+}
+
+hipError_t launch_lamb_norms(const LambBatch& b, const LambHyper& hp, float* partials,
+                             double* norms, hipStream_t s) {
+  const int nblk = b.blk_start[b.ntensors];
+  hipLaunchKernelGGL(lamb_pass_a, dim3(nblk), dim3(kLambThreads), 0, s, b, hp, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lamb_finalize_norms, dim3(b.ntensors), dim3(kFinThreads), 0, s, b,
+                     (const float*)partials, norms);
+  return hipGetLastError();
+}
+
+hipError_t launch_lamb_apply(const LambBatch& b, const LambHyper& hp, const double* norms,
+                             float* ratios, float* ratios_out, hipStream_t s) {
+  hipLaunchKernelGGL(lamb_ratios_from_norms, dim3(1), dim3(64), 0, s, b.ntensors, norms, ratios,
+                     ratios_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nblk = b.blk_start[b.ntensors];
   hipLaunchKernelGGL(lamb_pass_b, dim3(nblk), dim3(kLambThreads), 0, s, b, hp,
                      (const float*)ratios);
   return hipGetLastError();

@@ -131,3 +131,78 @@ class LambState:
     def set_grads(self, grads: list):
         for p, g in zip(self.params, grads):
             p["g"].copy_(torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to(p["g"].dtype))
+
+
+def shard_bounds(n: int, n_shards: int, align: int = 8) -> list:
+    """Contiguous element ranges of n over n_shards ranks, every start a
+    multiple of `align` (16-byte aligned fp32 and bf16 views); the last
+    ranks may be shorter or empty."""
+    per = -(-n // n_shards)
+    per = -(-per // align) * align
+    return [(min(n, r * per), min(n, (r + 1) * per)) for r in range(n_shards)]
+
+
+class ShardedLamb:
+    """ZeRO-2 sharded LAMB over a list of LAMB parameter dicts (w, g, m, v,
+    optional w_bf16, weight_decay; e.g. LambState.params): rank r owns
+    range r of every tensor (views into the same device tensors).  Each
+    rank's shard step is lamb_shard_norms, a sum of the per-rank norms (the
+    data-parallel all-reduce), then lamb_shard_apply."""
+
+    def __init__(self, all_params: list, n_shards: int):
+        self.ranks = []
+        nt = len(all_params)
+        device = all_params[0]["w"].device
+        for r in range(n_shards):
+            params = []
+            for p in all_params:
+                a, b = shard_bounds(p["w"].numel(), n_shards)[r]
+                # element ranges of the flattened (contiguous) tensors
+                q = {k: p[k].view(-1)[a:b] for k in ("w", "g", "m", "v")}
+                if p.get("w_bf16") is not None:
+                    q["w_bf16"] = p["w_bf16"].view(-1)[a:b]
+                q["weight_decay"] = p["weight_decay"]
+                params.append(q)
+            # ranks with an empty range of some tensor pass that tensor with
+            # n = 0 nowhere: such a rank keeps only its non-empty tensors
+            keep = [i for i, q in enumerate(params) if q["w"].numel() > 0]
+            desc = B.lamb_tensors([params[i] for i in keep]) if keep else None
+            scratch = (torch.empty(B.lamb_scratch_bytes(desc), dtype=torch.uint8, device=device)
+                       if keep else None)
+            self.ranks.append(dict(keep=keep, desc=desc, scratch=scratch, params=params,
+                                   norms=torch.zeros(2 * nt, dtype=torch.float64, device=device)))
+        self.ratios = torch.empty(nt, dtype=torch.float32, device=device)
+
+    def norms(self, rank, step, beta1, beta2, eps, stream=None):
+        """This rank's first half; returns its fp64 [2 n_tensors] norms."""
+        R = self.ranks[rank]
+        R["norms"].zero_()
+        if R["keep"]:
+            part = torch.empty(2 * len(R["keep"]), dtype=torch.float64, device=R["norms"].device)
+            B.lamb_shard_norms(R["desc"], beta1, beta2, eps, step, part, R["scratch"], stream)
+            idx = torch.tensor([[2 * i, 2 * i + 1] for i in R["keep"]],
+                               device=part.device).reshape(-1)
+            R["norms"].index_copy_(0, idx, part)
+        return R["norms"]
+
+    def apply(self, rank, total, step, lr, beta1, beta2, eps, stream=None):
+        """This rank's second half with the norms summed over all ranks."""
+        R = self.ranks[rank]
+        if not R["keep"]:
+            return
+        idx = torch.tensor([[2 * i, 2 * i + 1] for i in R["keep"]], device=total.device).reshape(-1)
+        sub = total.index_select(0, idx).contiguous()
+        ratios = torch.empty(len(R["keep"]), dtype=torch.float32, device=total.device)
+        B.lamb_shard_apply(R["desc"], lr, beta1, beta2, eps, step, sub, ratios, R["scratch"],
+                           stream)
+        self.ratios.index_copy_(0, torch.tensor(R["keep"], device=total.device), ratios)
+
+    def step(self, step, lr, beta1, beta2, eps, stream=None):
+        """All ranks on this one device in turn; the sum stands in for the
+        all-reduce between the halves."""
+        total = None
+        for r in range(len(self.ranks)):
+            n = self.norms(r, step, beta1, beta2, eps, stream).clone()
+            total = n if total is None else total + n
+        for r in range(len(self.ranks)):
+            self.apply(r, total, step, lr, beta1, beta2, eps, stream)
