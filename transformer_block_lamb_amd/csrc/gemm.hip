@@ -12,10 +12,11 @@
 // bf16 path (gfx950 MFMA): 256x256 output tile per workgroup of 8 waves (two
 // per SIMD, so one wave's LDS reads, load issue and waits overlap the
 // other's MFMAs), each wave a 128x64 sub-tile of 4x2
-// v_mfma_f32_32x32x16_bf16 blocks with 128 fp32 accumulators; K step 64.  Operand tiles go from memory
-// straight into LDS (buffer loads with the LDS bit, no register staging)
-// through a 2-stage ring: the loads of the next K tile are in flight for a
-// whole tile of MFMAs.  M/N-contiguous operands stay in that layout in LDS and are
+// v_mfma_f32_32x32x16_bf16 blocks with 128 fp32 accumulators; K step 64.
+// Operand tiles go from memory straight into LDS (buffer loads with the LDS
+// bit, no register staging) through a ring of five 32 KB slots, which keeps
+// every A tile in flight for two tiles of MFMAs and every B tile for one.
+// M/N-contiguous operands stay in that layout in LDS and are
 // read with the transposing LDS read (ds_read_b64_tr_b16) into the K-major
 // MFMA fragments.  Edges are masked by the buffer unit's range check (zero
 // fill), so any M, N, K is accepted.
@@ -34,9 +35,9 @@ namespace ptb {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kStages = 2;                    // K tiles resident in LDS (2 x 64 KB)
-constexpr int kOpBytes = BM * BK * 2;         // one operand tile, 32 KB
-constexpr int kStageBytes = 2 * kOpBytes;     // A tile, then B tile
+constexpr int kOpBytes = BM * BK * 2;         // one operand K tile, 32 KB (one LDS slot)
+constexpr int kSlots = 5;                     // operand slots in LDS (5 x 32 KB = 160 KB)
+constexpr int kSkAlign = 2;                   // stream-K ranges start on even iterations
 constexpr int kWaves = 8;                     // 2 per SIMD; wave grid 2 (M) x 4 (N)
 constexpr int kGemmThreads = 64 * kWaves;
 constexpr int kGroupM = 8;
@@ -218,7 +219,6 @@ __device__ __forceinline__ void tile_coords(int bid, int ntm, int ntn, const int
 //   P ^ (2 (k&3)), so the transposing fragment reads (ds_read_b64_tr_b16,
 //   4 K rows x 32 bytes per 16 lanes) hit distinct banks.
 constexpr int kDmaPerOp = kOpBytes / (kGemmThreads * 16);  // DMA instructions per lane
-constexpr int kDmaPerTile = 2 * kDmaPerOp;
 
 
 template <int LAY>
@@ -411,10 +411,10 @@ struct GemmArgs {
 constexpr int kPartialFloats = BM * BN;  // one partial tile in ws
 
 // First iteration of stream-K worker w (w == grid: end of the range);
-// rounded down to a multiple of kStages so segments are whole rounds.
+// rounded down to a multiple of kSkAlign.
 __host__ __device__ inline int64_t sk_lo(const GemmArgs& g, int w) {
   if (w >= g.grid) return g.sk_base + g.sk_iters;
-  return g.sk_base + (((int64_t)w * g.sk_iters / g.grid) & ~(int64_t)(kStages - 1));
+  return g.sk_base + (((int64_t)w * g.sk_iters / g.grid) & ~(int64_t)(kSkAlign - 1));
 }
 // The stream-K worker whose range holds iteration it.
 __device__ inline int sk_owner(const GemmArgs& g, int64_t it) {
@@ -506,29 +506,31 @@ __device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int l
   return ((((wave * 4 + i) * 2 + j) * 4 + r4) * 64 + lane) * 4;
 }
 
-// Main loop of one segment (K iterations kb .. ke of a tile): a two-stage
-// LDS pipeline over K tiles t (tiles nk1.. of a two-pass tile read a2).
-// Each tile is four phases of 16 MFMAs (one K=16 step each); every phase
-// reads the next step's fragments while it multiplies.  After the third
-// phase each wave waits for its own loads of tile t+1 and the workgroup
-// meets at the single barrier of the tile: from then on tile t's stage is
-// free, so the fourth phase reads tile t+1's first fragments and issues
-// tile t+2's loads into tile t's stage, a whole tile ahead of their use (for
-// an M/N-contiguous A only the A half; the B half follows in the first phase
-// of tile t+1).
-// Tiles past ke load zeros (no memory traffic), so the body has no
-// branches; the loop is unrolled by the number of stages so every LDS
-// address is static, and runs whole rounds of kStages tiles (an exit inside
-// a round makes the accumulators live across several loop exits, which
-// spills them).
+// Main loop of one segment (K iterations kb .. ke of a tile; iterations
+// nk1.. of a two-pass tile read a2).  Operand K tiles A_t and B_t (32 KB
+// each) rotate through five LDS slots in the order A0 B0 A1 B1 A2 B2 ...,
+// so while tile t is multiplied, tile t+1 is resident or landing and A_{t+2}
+// is in flight: A tiles are loaded two tiles ahead of use and B tiles one,
+// which halves the data each per-tile barrier waits for.  Each tile is four
+// phases of 16 MFMAs (one K=16 step each); every phase reads the next step's
+// fragments while it multiplies.  The first phase issues A_{t+2} into B_{t-1}'s
+// slot; after the third, each wave waits for its own loads of tile t+1 (all
+// but A_{t+2}) and the workgroup meets at the tile's only barrier; the
+// fourth phase reads tile t+1's first fragments and issues B_{t+2} into
+// A_t's slot.  The slot pattern repeats every five tiles, so the loop is
+// unrolled by five and every LDS address is static; tiles past ke load
+// zeros (no memory traffic) and skip their MFMAs, with the barriers and
+// loads kept so every wave's load count stays in step.
 template <int ALAY, int BLAY, class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
-  // one array per stage, so the compiler sees that loads into one stage do
+  // one array per slot, so the compiler sees that loads into one slot do
   // not alias fragment reads from another
-  __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
-  static_assert(kStages == 2, "stage arrays");
-  static_assert(4 * kStageBlk * 4 <= kStageBytes, "epilogue staging");
+  __shared__ __attribute__((aligned(1024))) char s0[kOpBytes];
+  __shared__ __attribute__((aligned(1024))) char s1[kOpBytes];
+  __shared__ __attribute__((aligned(1024))) char s2[kOpBytes];
+  __shared__ __attribute__((aligned(1024))) char s3[kOpBytes];
+  __shared__ __attribute__((aligned(1024))) char s4[kOpBytes];
+  static_assert(kSlots == 5, "slot arrays");
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, g.a_bytes);
   const __amdgpu_buffer_rsrc_t ra2 = make_rsrc(g.a2 != nullptr ? g.a2 : g.a, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, g.b_bytes);
@@ -538,13 +540,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   FragReader<BLAY, 2, 64> frb;
   fra.init(lane, wm);
   frb.init(lane, wn);
-  float* stage = reinterpret_cast<float*>((wave < 4 ? st0 : st1) + (wave & 3) * (2 * kStageBlk * 4));
-  static_assert(4 * 2 * kStageBlk * 4 <= kStageBytes, "epilogue staging");
+  float* stage = reinterpret_cast<float*>((wave < 3 ? s0 : wave < 6 ? s1 : s2) +
+                                          (wave % 3) * (2 * kStageBlk * 4));
+  static_assert(3 * 2 * kStageBlk * 4 <= kOpBytes, "epilogue staging");
   constexpr int kReads = (ALAY == kKContig ? 4 : 8) + (BLAY == kKContig ? 2 : 4);
-  // When to issue tile t+2's loads (measured per layout): all right after
-  // the barrier of tile t when A is K-contiguous; for an M/N-contiguous A the
-  // B half one phase later, which spreads the issue.
-  constexpr bool kSplitIssue = ALAY == kMNContig;
   const int nk1 = g.sc.nk1;
 
   // segment source: whole tiles first, then (sk) this worker's range
@@ -602,57 +601,58 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       da.issue(second ? ra2 : ra, st, wave, second ? t - nk1 : t, t < ke ? g.K : 0);
     };
     auto issue_b = [&](char* st, int t) {
-      db.issue(rb, st + kOpBytes, wave, t >= nk1 ? t - nk1 : t, t < ke ? g.K : 0);
+      db.issue(rb, st, wave, t >= nk1 ? t - nk1 : t, t < ke ? g.K : 0);
     };
     bf16x8_t fa[2][4], fb[2][2];
-    auto tile = [&](char* cur, char* nxt, int t) {
-      fra.read(fa[1], cur, 1);
-      frb.read(fb[1], cur + kOpBytes, 1);
-      if constexpr (kSplitIssue) {
-        issue_b(nxt, t + 1);  // second half of tile t+1's loads
+    // Tile t: A_t in slot ca, B_t in cb, tile t+1 in na / nb; sa is
+    // B_{t-1}'s slot, which takes A_{t+2}.  (The loads sit inside the
+    // branches so they interleave with the MFMAs.)
+    auto tile = [&](char* ca, char* cb, char* na, char* nb, char* sa, int t) {
+      const bool live = t < ke;
+      if (live) {
+        issue_a(sa, t + 2);
+        fra.read(fa[1], ca, 1);
+        frb.read(fb[1], cb, 1);
         mma_step(acc, fa[0], fb[0]);
         interleave<kReads, kDmaPerOp, 2>();
-      } else {
+        fra.read(fa[0], ca, 2);
+        frb.read(fb[0], cb, 2);
+        mma_step(acc, fa[1], fb[1]);
+        interleave<kReads, 0, 1>();
+        fra.read(fa[1], ca, 3);
+        frb.read(fb[1], cb, 3);
         mma_step(acc, fa[0], fb[0]);
         interleave<kReads, 0, 1>();
-      }
-      fra.read(fa[0], cur, 2);
-      frb.read(fb[0], cur + kOpBytes, 2);
-      mma_step(acc, fa[1], fb[1]);
-      interleave<kReads, 0, 1>();
-      fra.read(fa[1], cur, 3);
-      frb.read(fb[1], cur + kOpBytes, 3);
-      mma_step(acc, fa[0], fb[0]);
-      interleave<kReads, 0, 1>();
-      // tile t+1 has landed and every wave is done reading tile t
-      wait_barrier<0>();
-      fra.read(fa[0], nxt, 0);
-      frb.read(fb[0], nxt + kOpBytes, 0);
-      issue_a(cur, t + 2);  // tile t+2's loads (with kSplitIssue: the A half)
-      if constexpr (kSplitIssue) {
-        mma_step(acc, fa[1], fb[1]);
-        interleave<kReads, kDmaPerOp, 2>();
       } else {
-        issue_b(cur, t + 2);
+        issue_a(sa, t + 2);
+      }
+      // A_{t+1} and B_{t+1} have landed (A_{t+2}, issued last, may still be
+      // in flight) and every wave is done reading tile t
+      wait_barrier<kDmaPerOp>();
+      fra.read(fa[0], na, 0);
+      frb.read(fb[0], nb, 0);
+      if (live) {
+        issue_b(ca, t + 2);
         mma_step(acc, fa[1], fb[1]);
-        interleave<kReads, kDmaPerTile, 1>();
+        interleave<kReads, kDmaPerOp, 1>();
+      } else {
+        issue_b(ca, t + 2);
       }
     };
 
-    issue_a(st0, kb);
-    issue_b(st0, kb);
-    issue_a(st1, kb + 1);
-    if constexpr (kSplitIssue) {
-      wait_barrier<kDmaPerOp>();
-    } else {
-      issue_b(st1, kb + 1);
-      wait_barrier<kDmaPerTile>();
-    }
-    fra.read(fa[0], st0, 0);
-    frb.read(fb[0], st0 + kOpBytes, 0);
-    for (int t = kb; t < ke; t += kStages) {
-      tile(st0, st1, t);
-      tile(st1, st0, t + 1);
+    issue_a(s0, kb);
+    issue_b(s1, kb);
+    issue_a(s2, kb + 1);
+    issue_b(s3, kb + 1);
+    wait_barrier<2 * kDmaPerOp>();
+    fra.read(fa[0], s0, 0);
+    frb.read(fb[0], s1, 0);
+    for (int t = kb; t < ke; t += kSlots) {
+      tile(s0, s1, s2, s3, s4, t);
+      tile(s2, s3, s4, s0, s1, t + 1);
+      tile(s4, s0, s1, s2, s3, t + 2);
+      tile(s1, s2, s3, s4, s0, t + 3);
+      tile(s3, s4, s0, s1, s2, t + 4);
     }
     __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS
     __syncthreads();
@@ -835,7 +835,7 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
   // counts twice, and alone takes two units).
   const int G = persistent_grid();
   const int64_t total = g.sc.start(tiles);
-  if (G >= 8 && g.ws != nullptr && d.ws_bytes >= kGemmWsBytes && total >= 2 * (int64_t)G * kStages) {
+  if (G >= 8 && g.ws != nullptr && d.ws_bytes >= kGemmWsBytes && total >= 2 * (int64_t)G * kSkAlign) {
     const int64_t units = tiles + (int64_t)nh * ntm;  // in single-pass-tile units
     int64_t dp_rounds = (units + G - 1) / G;
     if (nh > 0 && dp_rounds < 2) dp_rounds = 2;
