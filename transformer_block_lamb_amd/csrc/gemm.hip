@@ -223,45 +223,61 @@ constexpr int kDmaPerOp = kOpBytes / (kGemmThreads * 16);  // DMA instructions p
 
 template <int LAY>
 struct DmaOperand {
-  // Piece i of this lane lies at base + i * istep bytes, K index kin + i * ikstep;
-  // `valid` bit i: its row exists.  (The swizzle makes kin the same for every
-  // piece of a K-contiguous tile, and the row the same for every piece of an
-  // M/N-contiguous tile.)
-  uint32_t base, istep, kstep;
+  // voff[i]: byte offset of this lane's piece i in K tile 0, or kOutOfRange
+  // when its row does not exist; K tile kt adds kt * kstep, which is the
+  // same for every lane and goes into the scalar offset, so a full tile's
+  // loads write no vector registers.  (A vector register that an
+  // outstanding LDS-bound load used as its address is not rewritten before
+  // that load completes, so per-tile address arithmetic would make the
+  // next write to such a register wait for the load.)  kin, ikstep: K
+  // index of piece 0 and the step per piece, for the masked edge tiles.
+  uint32_t voff[kDmaPerOp];
+  uint32_t kstep;
   int kin, ikstep;
-  uint32_t valid;
   __device__ __forceinline__ void init(int wave, int lane, int r0, int rows, int64_t ld) {
-    valid = 0;
     if (LAY == kKContig) {
-      const int row = 8 * wave + (lane >> 3);   // piece 0; piece i adds 64 i rows
+      const int row = 8 * wave + (lane >> 3);   // piece 0; piece i adds 8 kWaves i rows
       kin = 8 * ((lane & 7) ^ ((row >> 1) & 7));
       ikstep = 0;
-      base = (uint32_t)(((int64_t)(r0 + row) * ld + kin) * 2);
-      istep = (uint32_t)(64 * ld * 2);
+      const uint32_t base = (uint32_t)(((int64_t)(r0 + row) * ld + kin) * 2);
 #pragma unroll
-      for (int i = 0; i < kDmaPerOp; ++i) valid |= (r0 + row + 64 * i < rows ? 1u : 0u) << i;
+      for (int i = 0; i < kDmaPerOp; ++i)
+        voff[i] = r0 + row + 8 * kWaves * i < rows
+                      ? base + (uint32_t)(i * 8 * kWaves * ld * 2) : kOutOfRange;
       kstep = (uint32_t)(BK * 2);
     } else {
-      kin = 2 * wave + (lane >> 5);             // piece 0; piece i adds 16 i K rows
-      ikstep = 16;
+      kin = 2 * wave + (lane >> 5);             // piece 0; piece i adds 2 kWaves i K rows
+      ikstep = 2 * kWaves;
       const int q = lane & 31;
       const int row = 8 * (2 * ((q >> 1) ^ (2 * (kin & 3))) + (q & 1));
-      base = (uint32_t)(((int64_t)kin * ld + r0 + row) * 2);
-      istep = (uint32_t)(16 * ld * 2);
-      valid = r0 + row < rows ? (1u << kDmaPerOp) - 1 : 0u;
+      const uint32_t base = (uint32_t)(((int64_t)kin * ld + r0 + row) * 2);
+#pragma unroll
+      for (int i = 0; i < kDmaPerOp; ++i)
+        voff[i] = r0 + row < rows ? base + (uint32_t)(i * ikstep * ld * 2) : kOutOfRange;
       kstep = (uint32_t)(BK * ld * 2);
     }
   }
-  // K tile kt of the operand into LDS at `op`; pieces at K >= klim load zeros.
+  // K tile kt of the operand into LDS at `op`.  RAGGED (K is not a
+  // multiple of BK): pieces at K >= klim load zeros, through per-lane
+  // address selects; otherwise every tile is whole and the loads use the
+  // fixed per-lane offsets plus a scalar tile offset.
+  template <bool RAGGED>
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* op, int wave, int kt,
                                         int klim) const {
-    const uint32_t b = base + (uint32_t)kt * kstep;
+    if constexpr (!RAGGED) {
+      const uint32_t so = (uint32_t)kt * kstep;
 #pragma unroll
-    for (int i = 0; i < kDmaPerOp; ++i) {
-      const bool ok = ((valid >> i) & 1u) && kt * BK + kin + i * ikstep < klim;
-      const uint32_t off = ok ? b + (uint32_t)i * istep : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(op + (i * kWaves + wave) * 1024), 16,
-                                               off, 0, 0, 0);
+      for (int i = 0; i < kDmaPerOp; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(op + (i * kWaves + wave) * 1024),
+                                                 16, voff[i], so, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kDmaPerOp; ++i) {
+        const bool ok = voff[i] != kOutOfRange && kt * BK + kin + i * ikstep < klim;
+        const uint32_t off = ok ? voff[i] + (uint32_t)kt * kstep : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(op + (i * kWaves + wave) * 1024),
+                                                 16, off, 0, 0, 0);
+      }
     }
   }
 };
@@ -292,12 +308,16 @@ struct FragReader {
   __device__ __forceinline__ void read(bf16x8_t (&f)[NF], const char* op, int ks) const {
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
+      // every address is the slot base plus one integer offset (a pointer
+      // formed from another pointer can lose the slot's alias scope, and
+      // the compiler then waits for all loads in flight before the read)
       if (LAY == kKContig) {
-        f[i] = *reinterpret_cast<const bf16x8_t*>(op + off[ks] + i * 4096);
+        f[i] = *reinterpret_cast<const bf16x8_t*>(&op[off[ks] + i * 4096]);
       } else {
-        const char* p = op + off[i] + ks * 8192;
-        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)p);
-        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(p + 2048));
+        const int o = off[i] + ks * 8192;
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)&op[o]);
+        const bf16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)&op[o + 2048]);
         f[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
@@ -518,10 +538,11 @@ __device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int l
 // but A_{t+2}) and the workgroup meets at the tile's only barrier; the
 // fourth phase reads tile t+1's first fragments and issues B_{t+2} into
 // A_t's slot.  The slot pattern repeats every five tiles, so the loop is
-// unrolled by five and every LDS address is static; tiles past ke load
-// zeros (no memory traffic) and skip their MFMAs, with the barriers and
-// loads kept so every wave's load count stays in step.
-template <int ALAY, int BLAY, class Epi>
+// unrolled by five and every LDS address is static; tiles past ke skip
+// their MFMAs but keep their barriers and loads (of tile ke-1) so every
+// wave's load count stays in step with the waits.  RAGGED: K is not a
+// multiple of BK, so the last K tile masks its loads lane by lane.
+template <int ALAY, int BLAY, bool RAGGED, class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
   // one array per slot, so the compiler sees that loads into one slot do
   // not alias fragment reads from another
@@ -596,12 +617,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // Tiles past ke are never multiplied, but their loads keep every wave's
+    // load count in step with the waits: they reload tile ke-1 (in L2).
     auto issue_a = [&](char* st, int t) {
-      const bool second = t >= nk1;
-      da.issue(second ? ra2 : ra, st, wave, second ? t - nk1 : t, t < ke ? g.K : 0);
+      const int u = t < ke ? t : ke - 1;
+      const bool second = u >= nk1;
+      da.template issue<RAGGED>(second ? ra2 : ra, st, wave, second ? u - nk1 : u, g.K);
     };
     auto issue_b = [&](char* st, int t) {
-      db.issue(rb, st, wave, t >= nk1 ? t - nk1 : t, t < ke ? g.K : 0);
+      const int u = t < ke ? t : ke - 1;
+      db.template issue<RAGGED>(rb, st, wave, u >= nk1 ? u - nk1 : u, g.K);
     };
     bf16x8_t fa[2][4], fb[2][2];
     // Tile t: A_t in slot ca, B_t in cb, tile t+1 in na / nb; sa is
@@ -880,12 +905,20 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
         }
       }
     }
-    hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, Epi>), dim3(tiles), dim3(kGemmThreads), 0, s, g,
-                       epi);
+    if (d.K % BK == 0)
+      hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, false, Epi>), dim3(tiles), dim3(kGemmThreads),
+                         0, s, g, epi);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, true, Epi>), dim3(tiles), dim3(kGemmThreads),
+                         0, s, g, epi);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, Epi>), dim3(g.grid), dim3(kGemmThreads), 0, s, g,
-                     epi);
+  if (d.K % BK == 0)
+    hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, false, Epi>), dim3(g.grid), dim3(kGemmThreads),
+                       0, s, g, epi);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, true, Epi>), dim3(g.grid), dim3(kGemmThreads), 0,
+                       s, g, epi);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((gemm_fixup_kernel<Epi>), dim3(4 * (tiles - g.dp_tiles)), dim3(kGemmThreads), 0,
