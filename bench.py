@@ -45,6 +45,8 @@ def parse():
                    help="skip timing the fp64 CPU oracle")
     p.add_argument("--no-serial", action="store_true",
                    help="skip timing the serial pre-LN block on the same workload")
+    p.add_argument("--no-lamb-shard", action="store_true",
+                   help="skip timing one data-parallel rank's sharded LAMB")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run one plain device-to-device copy of MIB MiB and exit (the "
@@ -127,19 +129,26 @@ def time_serial(cfg, inputs, args, ptb_ms):
 def time_lamb_shard(params, args, dp=8):
     """One data-parallel rank's half-steps of ZeRO-2 sharded LAMB (rank 0 of
     `dp`, its 1/dp range of every tensor): lamb_shard_norms then
-    lamb_shard_apply.  The all-reduce of the 12 norms between them is a
-    collective across ranks and is not part of the timed kernels."""
+    lamb_shard_apply, called directly on the rank's descriptors.  The
+    all-reduce of the 12 norms between them is a collective across ranks and
+    is not part of the timed kernels (the rank's own norms stand in for the
+    sum)."""
     import numpy as np
     import torch
+    from transformer_block_lamb_amd import binding as B
     from transformer_block_lamb_amd.device import ShardedLamb
     from transformer_block_lamb_amd.synth import LAMB_HPARAMS
     hp = LAMB_HPARAMS
     sh = ShardedLamb(params, dp)
-    mine = sh.ranks[0]["params"]
+    R = sh.ranks[0]
+    assert len(R["keep"]) == len(params)  # every tensor reaches rank 0
+    norms = torch.empty(2 * len(params), dtype=torch.float64, device="cuda")
+    ratios = torch.empty(len(params), dtype=torch.float32, device="cuda")
 
     def half_steps(it):
-        n = sh.norms(0, it, hp["beta1"], hp["beta2"], hp["eps"])
-        sh.apply(0, n, it, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"])
+        B.lamb_shard_norms(R["desc"], hp["beta1"], hp["beta2"], hp["eps"], it, norms, R["scratch"])
+        B.lamb_shard_apply(R["desc"], hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], it, norms,
+                           ratios, R["scratch"])
 
     for it in range(1, args.warmup + 1):
         half_steps(it)
@@ -151,8 +160,8 @@ def time_lamb_shard(params, args, dp=8):
         ev[k][1].record()
     torch.cuda.synchronize()
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    nb = lamb_bytes(mine)
-    return {"dp": dp, "rank_params": int(sum(p["w"].numel() for p in mine)),
+    nb = lamb_bytes(R["params"])
+    return {"dp": dp, "rank_params": int(sum(p["w"].numel() for p in R["params"])),
             "ms": round(ms, 4), "gbps": round(nb / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(nb / (ms * 1e-3) / PEAK_HBM, 4)}
 
@@ -276,7 +285,7 @@ def main():
     serial = None
     if not args.no_serial:
         serial = time_serial(cfg, inputs, args, fwd_ms + bwd_ms)
-    lamb_shard = time_lamb_shard(params, args)
+    lamb_shard = None if args.no_lamb_shard else time_lamb_shard(params, args)
 
     flops = stage_flops(cfg)
     n_mat = (3 * A + F) * cfg.hidden + (A + F) * cfg.hidden
@@ -308,12 +317,14 @@ def main():
         "fwd_bwd_ms_min": round(float(np.min(fb_each)), 4),
         "lamb_gbps": round(lb / (lamb_ms * 1e-3) / 1e9, 1),
         "lamb_hbm_frac": round(lb / (lamb_ms * 1e-3) / PEAK_HBM, 4),
-        "lamb_bytes": lb, "lamb_zero2_rank": lamb_shard,
+        "lamb_bytes": lb,
         "executed_tflops": round(executed, 2),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4),
         "stages_ms": {n: round(v, 4) for n, v in per_stage.items()},
         "roofline": roofline,
     }
+    if lamb_shard is not None:
+        out["lamb_zero2_rank"] = lamb_shard
     if serial is not None:
         serial["model_tflops"] = round(model_flops / ((serial["fwd_ms"] + serial["bwd_ms"]) * 1e-3)
                                        / 1e12, 2)
