@@ -28,6 +28,8 @@
 //     transposed formulation of the forward.
 // fp32 path: one thread per query (or key) looping over its window; it serves
 // the fp32 workload only.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -59,39 +61,74 @@ constexpr int kTileLd = D + (D == 128 ? 16 : 8);
 // goes from memory straight into LDS with buffer loads that carry the LDS
 // bit: one wave instruction writes 1 KB of LDS, lane L's 16 bytes at byte
 // 16 L, so the row-major LDS tile (kTileLd<D> elements per row) is covered
-// by SL = kTileLd<D> / 8 instructions.  Lanes that land on a pad slot, or
-// on a row at or beyond `lim`, are steered out of the buffer's range and
-// write zeros.  Instruction n is issued by wave n % 4; slot[k] packs the
-// row (bits 5..) and 16-byte column (bits 0..4) of this lane's piece of
-// instruction wave + 4k, with pad slots pushed past every row limit.
+// by NI = kTileLd<D> / 8 instructions; instruction n is issued by wave
+// n % 4.  voff[k] is the byte offset, inside a tile, of this lane's piece
+// of instruction wave + 4k (kOutOfRange for a pad slot, which then loads
+// zeros); the tile's first row goes into the scalar offset, so whole tiles
+// load without writing any vector register (a vector register that an
+// outstanding LDS-bound load used as its address is not rewritten before
+// the load completes, and per-tile address arithmetic would stall on it).
+// RAGGED (the sequence is not a multiple of 64 rows): rows at or beyond
+// `lim` are steered out of the buffer's range lane by lane.
 template <int D>
 struct DmaRows {
   static constexpr int CH = D / 8, SL = kTileLd<D> / 8;
   static constexpr int NI = SL;             // 1 KB instructions per tile
   static constexpr int NW = (NI + 3) / 4;   // per wave, at most
-  int slot[NW];
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // instructions of one tile issued by wave w
+  static constexpr int count(int w) { return (NI - w + 3) / 4; }
+  uint32_t voff[NW];
+  int row[NW];
+  __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       const int s = (wave + 4 * k) * 64 + lane, r = s / SL, c = s - r * SL;
-      slot[k] = c < CH ? (r << 5) | c : (1 << 30);
+      row[k] = r;
+      voff[k] = c < CH ? (uint32_t)(((int64_t)r * ld + c * 8) * 2) : kOutOfRange;
     }
   }
+  template <bool RAGGED>
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, bf16_t* tile, int wave, int r0,
                                         int lim, int64_t ld) const {
+    const uint32_t so = (uint32_t)((int64_t)r0 * ld * 2);
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       const int n = wave + 4 * k;
       if (n < NI) {  // uniform over the wave
-        const int r = r0 + (slot[k] >> 5);
-        const uint32_t o = r < lim ? (uint32_t)r * (uint32_t)(ld * 2) + 16u * (slot[k] & 31)
-                                   : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + n * 512), 16, o, 0, 0,
-                                                 0);
+        if constexpr (!RAGGED) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + n * 512), 16, voff[k],
+                                                   so, 0, 0);
+        } else {
+          const uint32_t o =
+              voff[k] != kOutOfRange && r0 + row[k] < lim ? voff[k] + so : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + n * 512), 16, o, 0,
+                                                   0, 0);
+        }
       }
     }
   }
 };
+
+// K/V (or Q/dO) tiles in flight: three stages where they fit in LDS next to
+// each other (d <= 96), else two.  With three, the loads of tile t+2 are
+// issued while tile t is multiplied and tile t+1 may still be landing.
+template <int D>
+constexpr int kSwaStages = D <= 96 ? 3 : 2;
+
+// Waits until this wave has at most VM loads outstanding (the LDS-bound ones
+// included) and no LDS reads, then joins the workgroup barrier.  VM0 is
+// wave 0's allowance, VM1 the other waves' (wave 0 may issue more).
+template <int VM0, int VM1>
+__device__ __forceinline__ void tile_barrier(int wave) {
+  static_assert(VM0 < 64 && VM1 < 64, "vmcnt field");
+  __builtin_amdgcn_sched_barrier(0);
+  if (wave == 0)
+    __builtin_amdgcn_s_waitcnt((VM0 & 15) | ((VM0 >> 4) << 14) | (7 << 4));
+  else
+    __builtin_amdgcn_s_waitcnt((VM1 & 15) | ((VM1 >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // The buffer covering one sequence's rows of a D-column block: rows 0 ..
 // seq - 1 of a token-major matrix with leading dimension ld (the entry
@@ -118,14 +155,20 @@ __device__ __forceinline__ bf16x8_t ld_frag_tr(const bf16_t* tile, int row0, int
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Waits for this wave's outstanding loads (the LDS-bound ones included) and
-// LDS reads, then joins the workgroup barrier: after it every wave's tile
-// loads issued before it have landed in LDS.
-__device__ __forceinline__ void drain_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
+
+// Workgroup -> (row block, head, sequence) of a launch over every row block
+// of every head.  The hardware deals workgroups round-robin to the 8 XCDs;
+// the remap gives each XCD a contiguous range of (sequence, head, block), so
+// the row blocks of one head run on one XCD and share that head's K/V (or
+// Q/dO) tiles in its L2 instead of fetching them once per XCD.
+struct SwaBlock {
+  int blk, h, b;
+};
+__device__ __forceinline__ SwaBlock swa_block(int S, int H) {
+  const int total = gridDim.x, nb = (S + kBQ - 1) / kBQ, per = total >> 3;
+  int l = blockIdx.x;
+  if (l < (per << 3)) l = (l & 7) * per + (l >> 3);
+  return {l % nb, (l / nb) % H, l / (nb * H)};
 }
 
 // ------------------------------------------------------------------ forward
@@ -151,20 +194,23 @@ __device__ __forceinline__ void load_row_frags(bf16x8_t (&f)[D / 16], const bf16
 // while tile kt is multiplied.  The loop body is written out twice with the
 // two buffers swapped (the tile count is rounded up to even; the extra body
 // only joins the barrier) so that every LDS access names a fixed array.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool RAGGED>
 __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __restrict__ qkv,
                                                             int64_t ldq,
                                                             const bf16_t* __restrict__ qk_lo,
                                                             int64_t ldl, bf16_t* __restrict__ out,
                                                             int64_t ldo, float* __restrict__ lse,
                                                             int S, int H, int W, float sl2) {
-  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8;
-  __shared__ __attribute__((aligned(16))) bf16_t K0[TE], K1[TE], V0[TE], V1[TE];
-  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL];
-  const int h = blockIdx.y, b = blockIdx.z;
+  constexpr int NS = kSwaStages<D>;
+  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8, T3 = NS > 2 ? TE : 8,
+                TL3 = NS > 2 ? TL : 8;
+  __shared__ __attribute__((aligned(16))) bf16_t K0[TE], K1[TE], K2[T3], V0[TE], V1[TE], V2[T3];
+  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL], L2[TL3];
+  const SwaBlock sb = swa_block(S, H);
+  const int h = sb.h, b = sb.b;
   const int A = H * D;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int q0 = blockIdx.x * kBQ;
+  const int q0 = sb.blk * kBQ;
   const int qw = q0 + wave * 32;
   const int qi = qw + (lane & 31);
   const bf16_t* base = qkv + (int64_t)b * S * ldq;
@@ -175,21 +221,31 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(Kp, ldq, S, D), rv = rows_rsrc(Vp, ldq, S, D);
   const __amdgpu_buffer_rsrc_t rl =
       SPLIT ? rows_rsrc(lo_base + A + h * D, ldl, S, D) : rk;
-  DmaRows<D> dma;
-  dma.init(wave, lane);
+  DmaRows<D> dq_, dl_;
+  dq_.init(wave, lane, ldq);
+  if (SPLIT) dl_.init(wave, lane, ldl);
+  // loads per tile of wave 0 and of the others (the same for waves 1-3
+  // whenever three stages are used)
+  constexpr int NA = SPLIT ? 3 : 2;
+  constexpr int C0 = NA * DmaRows<D>::count(0), C1 = NA * DmaRows<D>::count(1);
+  static_assert(NS == 2 || (DmaRows<D>::count(1) == DmaRows<D>::count(3)), "load counts");
 
   const int qlast = min(q0 + kBQ, S) - 1;
   const int kt_lo = max(0, q0 - W + 1) / kBKV, kt_hi = qlast / kBKV;
+  // tiles past kt_hi reload tile kt_hi: they are never used, but every body
+  // issues the same loads, so the load counts the waits assume hold
   auto issue = [&](bf16_t* k, bf16_t* kl, bf16_t* v, int kt) {
-    dma.issue(rk, k, wave, kt * kBKV, S, ldq);
-    if (SPLIT) dma.issue(rl, kl, wave, kt * kBKV, S, ldl);
-    dma.issue(rv, v, wave, kt * kBKV, S, ldq);
+    const int r0 = min(kt, kt_hi) * kBKV;
+    dq_.template issue<RAGGED>(rk, k, wave, r0, S, ldq);
+    if (SPLIT) dl_.template issue<RAGGED>(rl, kl, wave, r0, S, ldl);
+    dq_.template issue<RAGGED>(rv, v, wave, r0, S, ldq);
   };
-  issue(K0, L0, V0, kt_lo);
 
   bf16x8_t qf[D / 16], qf_lo[D / 16];
   load_row_frags<D>(qf, Qp, ldq, qi, S, lane);
   if (SPLIT) load_row_frags<D>(qf_lo, lo_base + h * D, ldl, qi, S, lane);
+  issue(K0, L0, V0, kt_lo);
+  if (NS > 2) issue(K1, L1, V1, kt_lo + 1);
   f32x16_t o[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
@@ -198,10 +254,12 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   float m_run = -INFINITY, l_run = 0.f;
   const bool wave_live = qw < S;
 
+  // tile kt is in (Ks, Ks_lo, Vs); tile kt + NS - 1 goes into (nk, nl, nv),
+  // the stage tile kt - 1 used
   auto body = [&](const bf16_t* Ks, const bf16_t* Ks_lo, const bf16_t* Vs, bf16_t* nk,
                   bf16_t* nl, bf16_t* nv, int kt) {
-    drain_barrier();
-    if (kt < kt_hi) issue(nk, nl, nv, kt + 1);
+    tile_barrier<(NS - 2) * C0, (NS - 2) * C1>(wave);
+    issue(nk, nl, nv, kt + NS - 1);
     const int j0 = kt * kBKV;
     if (kt > kt_hi || !wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) return;
     const bool full = (j0 + kBKV - 1 <= qw) && (qw + 31 - j0 < W) && (j0 + kBKV <= S);
@@ -237,7 +295,7 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
     mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
     const float m_new = fmaxf(m_run, mblk);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     l_run *= alpha;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
@@ -249,7 +307,7 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[kh][r] = exp2f(st[kh][r] - m_use);
+        p[kh][r] = __builtin_amdgcn_exp2f(st[kh][r] - m_use);
         l_run += p[kh][r];
       }
 #pragma unroll
@@ -262,10 +320,19 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
           o[mb] = mfma32(ld_frag_tr<KLD>(Vs, kh * 32 + hf * 16, mb * 32, lane), pb, o[mb]);
       }
   };
-  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-    body(K0, L0, V0, K1, L1, V1, kt);
-    body(K1, L1, V1, K0, L0, V0, kt + 1);
+  if constexpr (NS == 2) {
+    for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+      body(K0, L0, V0, K1, L1, V1, kt);
+      body(K1, L1, V1, K0, L0, V0, kt + 1);
+    }
+  } else {
+    for (int kt = kt_lo; kt <= kt_hi; kt += 3) {
+      body(K0, L0, V0, K2, L2, V2, kt);
+      body(K1, L1, V1, K0, L0, V0, kt + 1);
+      body(K2, L2, V2, K1, L1, V1, kt + 2);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS when the workgroup ends
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qi < S) {
     const float inv = 1.0f / l_tot;
@@ -316,20 +383,24 @@ __global__ __launch_bounds__(256) void swa_rowdot(const T* __restrict__ d_o, int
 // log-sum-exp and D values of the next query tile ride in registers of the
 // first wave and are written to LDS just before the barrier that publishes
 // their tile.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool RAGGED>
 __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
     const bf16_t* __restrict__ qkv, int64_t ldq, const bf16_t* __restrict__ qk_lo, int64_t ldl,
     const bf16_t* __restrict__ d_o, int64_t ld_do,
     const float* __restrict__ lse, const float* __restrict__ dvec, bf16_t* __restrict__ dqkv,
     int64_t ldd, int S, int H, int W, float sl2, float scale) {
-  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8;
-  __shared__ __attribute__((aligned(16))) bf16_t Q0[TE], Q1[TE], O0[TE], O1[TE];
-  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL];
-  __shared__ __attribute__((aligned(16))) float ls0[kBKV], ls1[kBKV], dd0[kBKV], dd1[kBKV];
-  const int h = blockIdx.y, b = blockIdx.z;
+  constexpr int NS = kSwaStages<D>;
+  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8, T3 = NS > 2 ? TE : 8,
+                TL3 = NS > 2 ? TL : 8;
+  __shared__ __attribute__((aligned(16))) bf16_t Q0[TE], Q1[TE], Q2[T3], O0[TE], O1[TE], O2[T3];
+  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL], L2[TL3];
+  __shared__ __attribute__((aligned(16))) float ls0[kBKV], ls1[kBKV], ls2[kBKV];
+  __shared__ __attribute__((aligned(16))) float dd0[kBKV], dd1[kBKV], dd2[kBKV];
+  const SwaBlock sb = swa_block(S, H);
+  const int h = sb.h, b = sb.b;
   const int A = H * D;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int k0 = blockIdx.x * kBQ;
+  const int k0 = sb.blk * kBQ;
   const int kw = k0 + wave * 32;
   const int kj = kw + (lane & 31);
   const bf16_t* base = qkv + (int64_t)b * S * ldq;
@@ -342,29 +413,42 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
   const bf16_t* lo_base = SPLIT ? qk_lo + (int64_t)b * S * ldl : nullptr;
   const __amdgpu_buffer_rsrc_t rq = rows_rsrc(Qp, ldq, S, D), ro = rows_rsrc(dOp, ld_do, S, D);
   const __amdgpu_buffer_rsrc_t rl = SPLIT ? rows_rsrc(lo_base + h * D, ldl, S, D) : rq;
-  DmaRows<D> dma;
-  dma.init(wave, lane);
+  // the tile's log-sum-exp and D values (64 floats each) go to LDS with one
+  // 4-byte LDS-bound load per lane, issued by wave 0
+  const __amdgpu_buffer_rsrc_t rls = make_rsrc(lse_b, (uint32_t)S * 4u);
+  const __amdgpu_buffer_rsrc_t rdd = make_rsrc(dv_b, (uint32_t)S * 4u);
+  uint32_t lane4 = (uint32_t)lane * 4u;
+  asm volatile("" : "+v"(lane4));  // kept in one register, not recomputed per load
+  DmaRows<D> dq_, dl_, do_;
+  dq_.init(wave, lane, ldq);
+  if (SPLIT) dl_.init(wave, lane, ldl);
+  do_.init(wave, lane, ld_do);
+  constexpr int NA = SPLIT ? 3 : 2;
+  constexpr int C0 = NA * DmaRows<D>::count(0) + 2, C1 = NA * DmaRows<D>::count(1);
+  static_assert(NS == 2 || (DmaRows<D>::count(1) == DmaRows<D>::count(3)), "load counts");
 
   const int klast = min(k0 + kBQ, S) - 1;
   const int qt_lo = k0 / kBKV, qt_hi = min(S - 1, klast + W - 1) / kBKV;
-  float nls = 0.f, ndd = 0.f;  // next tile's lse and D, threads 0..63
-  auto issue = [&](bf16_t* q, bf16_t* ql, bf16_t* o, int qt) {
-    const int i0 = qt * kBKV;
-    dma.issue(rq, q, wave, i0, S, ldq);
-    if (SPLIT) dma.issue(rl, ql, wave, i0, S, ldl);
-    dma.issue(ro, o, wave, i0, S, ld_do);
-    if (threadIdx.x < kBKV) {
-      const int i = i0 + threadIdx.x;
-      nls = i < S ? lse_b[i] : 0.f;
-      ndd = i < S ? dv_b[i] : 0.f;
+  // tiles past qt_hi reload tile qt_hi (never used; keeps the load counts)
+  auto issue = [&](bf16_t* q, bf16_t* ql, bf16_t* o, float* ls, float* dd, int qt) {
+    const int i0 = min(qt, qt_hi) * kBKV;
+    dq_.template issue<RAGGED>(rq, q, wave, i0, S, ldq);
+    if (SPLIT) dl_.template issue<RAGGED>(rl, ql, wave, i0, S, ldl);
+    do_.template issue<RAGGED>(ro, o, wave, i0, S, ld_do);
+    if (wave == 0) {
+      const uint32_t so = (uint32_t)i0 * 4u;
+      const uint32_t vo = RAGGED && i0 + lane >= S ? kOutOfRange : lane4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rls, (lds_void_t*)ls, 4, vo, RAGGED ? 0 : so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rdd, (lds_void_t*)dd, 4, vo, RAGGED ? 0 : so, 0, 0);
     }
   };
-  issue(Q0, L0, O0, qt_lo);
 
   bf16x8_t kf[D / 16], vf[D / 16], kf_lo[D / 16];
   load_row_frags<D>(kf, Kp, ldq, kj, S, lane);
   load_row_frags<D>(vf, Vp, ldq, kj, S, lane);
   if (SPLIT) load_row_frags<D>(kf_lo, lo_base + A + h * D, ldl, kj, S, lane);
+  issue(Q0, L0, O0, ls0, dd0, qt_lo);
+  if (NS > 2) issue(Q1, L1, O1, ls1, dd1, qt_lo + 1);
   f32x16_t dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
@@ -372,11 +456,13 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
     for (int r = 0; r < 16; ++r) { dk[mb][r] = 0.f; dv[mb][r] = 0.f; }
   const bool wave_live = kw < S;
 
-  auto body = [&](const bf16_t* Qs, const bf16_t* Qs_lo, const bf16_t* dOs, float* lse_s,
-                  float* dv_s, bf16_t* nq, bf16_t* nql, bf16_t* no, int qt) {
-    if (threadIdx.x < kBKV) { lse_s[threadIdx.x] = nls * kLog2e; dv_s[threadIdx.x] = ndd; }
-    drain_barrier();
-    if (qt < qt_hi) issue(nq, nql, no, qt + 1);
+  // tile qt is in (Qs, Qs_lo, dOs, lse_s, dv_s); tile qt + NS - 1 goes into
+  // the n* arrays, the stage tile qt - 1 used
+  auto body = [&](const bf16_t* Qs, const bf16_t* Qs_lo, const bf16_t* dOs, const float* lse_s,
+                  const float* dv_s, bf16_t* nq, bf16_t* nql, bf16_t* no, float* nls, float* ndd,
+                  int qt) {
+    tile_barrier<(NS - 2) * C0, (NS - 2) * C1>(wave);
+    issue(nq, nql, no, nls, ndd, qt + NS - 1);
     const int i0 = qt * kBKV;
     if (qt > qt_hi || !wave_live || i0 > kw + 31 + W - 1 || i0 + kBKV - 1 < kw) return;
     const bool full = (i0 >= kw + 31) && (i0 + kBKV - 1 - kw < W) && (i0 + kBKV <= S);
@@ -406,7 +492,7 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pv = exp2f(s[r] * sl2 - lv[e]);
+          float pv = __builtin_amdgcn_exp2f(s[r] * sl2 - lv[e] * kLog2e);
           if (!full) {
             const int i = i0 + rb + e;
             if (!(visible(i, kj, W) && i < S)) pv = 0.f;
@@ -427,10 +513,19 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
       }
     }
   };
-  for (int qt = qt_lo; qt <= qt_hi; qt += 2) {
-    body(Q0, L0, O0, ls0, dd0, Q1, L1, O1, qt);
-    body(Q1, L1, O1, ls1, dd1, Q0, L0, O0, qt + 1);
+  if constexpr (NS == 2) {
+    for (int qt = qt_lo; qt <= qt_hi; qt += 2) {
+      body(Q0, L0, O0, ls0, dd0, Q1, L1, O1, ls1, dd1, qt);
+      body(Q1, L1, O1, ls1, dd1, Q0, L0, O0, ls0, dd0, qt + 1);
+    }
+  } else {
+    for (int qt = qt_lo; qt <= qt_hi; qt += 3) {
+      body(Q0, L0, O0, ls0, dd0, Q2, L2, O2, ls2, dd2, qt);
+      body(Q1, L1, O1, ls1, dd1, Q0, L0, O0, ls0, dd0, qt + 1);
+      body(Q2, L2, O2, ls2, dd2, Q1, L1, O1, ls1, dd1, qt + 2);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS when the workgroup ends
   if (kj < S) {
     bf16_t* row = dqkv + ((int64_t)b * S + kj) * ldd + h * D;
 #pragma unroll
@@ -451,19 +546,22 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
 
 // ------------------------------------------------------------------ dQ
 // K, K_lo and V tiles double-buffered in LDS as in the forward.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool RAGGED>
 __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
     const bf16_t* __restrict__ qkv, int64_t ldq, const bf16_t* __restrict__ qk_lo, int64_t ldl,
     const bf16_t* __restrict__ d_o, int64_t ld_do,
     const float* __restrict__ lse, const float* __restrict__ dvec, bf16_t* __restrict__ dqkv,
     int64_t ldd, int S, int H, int W, float sl2, float scale) {
-  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8;
-  __shared__ __attribute__((aligned(16))) bf16_t K0[TE], K1[TE], V0[TE], V1[TE];
-  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL];
-  const int h = blockIdx.y, b = blockIdx.z;
+  constexpr int NS = kSwaStages<D>;
+  constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8, T3 = NS > 2 ? TE : 8,
+                TL3 = NS > 2 ? TL : 8;
+  __shared__ __attribute__((aligned(16))) bf16_t K0[TE], K1[TE], K2[T3], V0[TE], V1[TE], V2[T3];
+  __shared__ __attribute__((aligned(16))) bf16_t L0[TL], L1[TL], L2[TL3];
+  const SwaBlock sb = swa_block(S, H);
+  const int h = sb.h, b = sb.b;
   const int A = H * D;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int q0 = blockIdx.x * kBQ;
+  const int q0 = sb.blk * kBQ;
   const int qw = q0 + wave * 32;
   const int qi = qw + (lane & 31);
   const bf16_t* base = qkv + (int64_t)b * S * ldq;
@@ -475,22 +573,32 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(Kp, ldq, S, D), rv = rows_rsrc(Vp, ldq, S, D);
   const __amdgpu_buffer_rsrc_t rl =
       SPLIT ? rows_rsrc(lo_base + A + h * D, ldl, S, D) : rk;
-  DmaRows<D> dma;
-  dma.init(wave, lane);
+  DmaRows<D> dq_, dl_;
+  dq_.init(wave, lane, ldq);
+  if (SPLIT) dl_.init(wave, lane, ldl);
+  // loads per tile of wave 0 and of the others (the same for waves 1-3
+  // whenever three stages are used)
+  constexpr int NA = SPLIT ? 3 : 2;
+  constexpr int C0 = NA * DmaRows<D>::count(0), C1 = NA * DmaRows<D>::count(1);
+  static_assert(NS == 2 || (DmaRows<D>::count(1) == DmaRows<D>::count(3)), "load counts");
 
   const int qlast = min(q0 + kBQ, S) - 1;
   const int kt_lo = max(0, q0 - W + 1) / kBKV, kt_hi = qlast / kBKV;
+  // tiles past kt_hi reload tile kt_hi: they are never used, but every body
+  // issues the same loads, so the load counts the waits assume hold
   auto issue = [&](bf16_t* k, bf16_t* kl, bf16_t* v, int kt) {
-    dma.issue(rk, k, wave, kt * kBKV, S, ldq);
-    if (SPLIT) dma.issue(rl, kl, wave, kt * kBKV, S, ldl);
-    dma.issue(rv, v, wave, kt * kBKV, S, ldq);
+    const int r0 = min(kt, kt_hi) * kBKV;
+    dq_.template issue<RAGGED>(rk, k, wave, r0, S, ldq);
+    if (SPLIT) dl_.template issue<RAGGED>(rl, kl, wave, r0, S, ldl);
+    dq_.template issue<RAGGED>(rv, v, wave, r0, S, ldq);
   };
-  issue(K0, L0, V0, kt_lo);
 
   bf16x8_t qf[D / 16], of[D / 16], qf_lo[D / 16];
   load_row_frags<D>(qf, Qp, ldq, qi, S, lane);
   load_row_frags<D>(of, dOp, ld_do, qi, S, lane);
   if (SPLIT) load_row_frags<D>(qf_lo, lo_base + h * D, ldl, qi, S, lane);
+  issue(K0, L0, V0, kt_lo);
+  if (NS > 2) issue(K1, L1, V1, kt_lo + 1);
   const float lse2 = qi < S ? lse[((int64_t)b * H + h) * S + qi] * kLog2e : 0.f;
   const float di = qi < S ? dvec[((int64_t)b * H + h) * S + qi] : 0.f;
   f32x16_t dq[D / 32];
@@ -502,8 +610,8 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
 
   auto body = [&](const bf16_t* Ks, const bf16_t* Ks_lo, const bf16_t* Vs, bf16_t* nk,
                   bf16_t* nl, bf16_t* nv, int kt) {
-    drain_barrier();
-    if (kt < kt_hi) issue(nk, nl, nv, kt + 1);
+    tile_barrier<(NS - 2) * C0, (NS - 2) * C1>(wave);
+    issue(nk, nl, nv, kt + NS - 1);
     const int j0 = kt * kBKV;
     if (kt > kt_hi || !wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) return;
     const bool full = (j0 + kBKV - 1 <= qw) && (qw + 31 - j0 < W) && (j0 + kBKV <= S);
@@ -526,7 +634,7 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = exp2f(st[r] * sl2 - lse2);
+        float pv = __builtin_amdgcn_exp2f(st[r] * sl2 - lse2);
         if (!full) {
           const int j = j0 + kh * 32 + mfma32_row(r, lane);
           if (!(visible(qi, j, W) && j < S)) pv = 0.f;
@@ -542,10 +650,19 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
       }
     }
   };
-  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-    body(K0, L0, V0, K1, L1, V1, kt);
-    body(K1, L1, V1, K0, L0, V0, kt + 1);
+  if constexpr (NS == 2) {
+    for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+      body(K0, L0, V0, K1, L1, V1, kt);
+      body(K1, L1, V1, K0, L0, V0, kt + 1);
+    }
+  } else {
+    for (int kt = kt_lo; kt <= kt_hi; kt += 3) {
+      body(K0, L0, V0, K2, L2, V2, kt);
+      body(K1, L1, V1, K0, L0, V0, kt + 1);
+      body(K2, L2, V2, K1, L1, V1, kt + 2);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS when the workgroup ends
   if (qi < S) {
     bf16_t* row = dqkv + ((int64_t)b * S + qi) * ldd + h * D;
 #pragma unroll
@@ -660,20 +777,31 @@ __global__ __launch_bounds__(128) void swa_bwd_dkdv_simt(
   for (int c = 0; c < D; ++c) { row[A + c] = dk[c] * scale; row[2 * A + c] = dv[c]; }
 }
 
+// Calls f(split, ragged) with both flags as compile-time constants.
+template <class F>
+void dispatch2(bool split, bool ragged, F&& f) {
+  using T = std::true_type;
+  using U = std::false_type;
+  if (split) {
+    if (ragged) f(T{}, T{}); else f(T{}, U{});
+  } else {
+    if (ragged) f(U{}, T{}); else f(U{}, U{});
+  }
+}
+
 template <int D>
 hipError_t fwd_d(int dtype, const SwaDesc& a, void* o, int64_t ldo, float* lse, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)D);
   if (dtype == 1) {
-    dim3 grid((a.seq + kBQ - 1) / kBQ, a.n_heads, a.batch);
+    dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
     const int64_t ldl = 2 * (int64_t)a.n_heads * D;
-    if (a.qk_lo != nullptr)
-      hipLaunchKernelGGL((swa_fwd_mfma<D, true>), grid, dim3(kSwaThreads), 0, s,
-                         (const bf16_t*)a.qkv, a.ld_qkv, (const bf16_t*)a.qk_lo, ldl,
-                         (bf16_t*)o, ldo, lse, a.seq, a.n_heads, a.window, scale * kLog2e);
-    else
-      hipLaunchKernelGGL((swa_fwd_mfma<D, false>), grid, dim3(kSwaThreads), 0, s,
-                         (const bf16_t*)a.qkv, a.ld_qkv, (const bf16_t*)nullptr, ldl,
-                         (bf16_t*)o, ldo, lse, a.seq, a.n_heads, a.window, scale * kLog2e);
+    auto go = [&](auto split, auto ragged) {
+      hipLaunchKernelGGL((swa_fwd_mfma<D, decltype(split)::value, decltype(ragged)::value>), grid,
+                         dim3(kSwaThreads), 0, s, (const bf16_t*)a.qkv, a.ld_qkv,
+                         (const bf16_t*)a.qk_lo, ldl, (bf16_t*)o, ldo, lse, a.seq, a.n_heads,
+                         a.window, scale * kLog2e);
+    };
+    dispatch2(a.qk_lo != nullptr, a.seq % kBKV != 0, go);
   } else {
     const int64_t n = (int64_t)a.batch * a.n_heads * a.seq;
     hipLaunchKernelGGL((swa_fwd_simt<D>), dim3((n + 127) / 128), dim3(128), 0, s,
@@ -693,28 +821,21 @@ hipError_t bwd_d(int dtype, const SwaDesc& a, const void* o, int64_t ldo, const 
     hipLaunchKernelGGL((swa_rowdot<bf16_t>), dim3((n + 255) / 256), dim3(256), 0, s,
                        (const bf16_t*)d_o, ld_do, (const bf16_t*)o, ldo, dvec, a.batch, a.seq,
                        a.n_heads, D);
-    dim3 grid((a.seq + kBQ - 1) / kBQ, a.n_heads, a.batch);
+    dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
     const int64_t ldl = 2 * (int64_t)a.n_heads * D;
     const bf16_t* lo = (const bf16_t*)a.qk_lo;
-    if (lo != nullptr) {
-      hipLaunchKernelGGL((swa_bwd_dkdv_mfma<D, true>), grid, dim3(kSwaThreads), 0, s,
+    auto go = [&](auto split, auto ragged) {
+      constexpr bool SP = decltype(split)::value, RG = decltype(ragged)::value;
+      hipLaunchKernelGGL((swa_bwd_dkdv_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
                          (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse,
                          (const float*)dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window,
                          scale * kLog2e, scale);
-      hipLaunchKernelGGL((swa_bwd_dq_mfma<D, true>), grid, dim3(kSwaThreads), 0, s,
+      hipLaunchKernelGGL((swa_bwd_dq_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
                          (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse,
                          (const float*)dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window,
                          scale * kLog2e, scale);
-    } else {
-      hipLaunchKernelGGL((swa_bwd_dkdv_mfma<D, false>), grid, dim3(kSwaThreads), 0, s,
-                         (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse,
-                         (const float*)dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window,
-                         scale * kLog2e, scale);
-      hipLaunchKernelGGL((swa_bwd_dq_mfma<D, false>), grid, dim3(kSwaThreads), 0, s,
-                         (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse,
-                         (const float*)dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window,
-                         scale * kLog2e, scale);
-    }
+    };
+    dispatch2(lo != nullptr, a.seq % kBKV != 0, go);
   } else {
     hipLaunchKernelGGL((swa_rowdot<float>), dim3((n + 255) / 256), dim3(256), 0, s,
                        (const float*)d_o, ld_do, (const float*)o, ldo, dvec, a.batch, a.seq,
