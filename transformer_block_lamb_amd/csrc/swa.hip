@@ -28,8 +28,6 @@
 //     transposed formulation of the forward.
 // fp32 path: one thread per query (or key) looping over its window; it serves
 // the fp32 workload only.
-#include <type_traits>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -87,17 +85,20 @@ struct DmaRows {
       voff[k] = c < CH ? (uint32_t)(((int64_t)r * ld + c * 8) * 2) : kOutOfRange;
     }
   }
-  template <bool RAGGED>
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, bf16_t* tile, int wave, int r0,
-                                        int lim, int64_t ld) const {
+  // `ragged` is a compile-time constant at every call site (inlined).
+  __device__ __forceinline__ void issue(bool ragged, __amdgpu_buffer_rsrc_t rs, bf16_t* tile,
+                                        int wave, int r0, int lim, int64_t ld) const {
     const uint32_t so = (uint32_t)((int64_t)r0 * ld * 2);
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       const int n = wave + 4 * k;
       if (n < NI) {  // uniform over the wave
-        if constexpr (!RAGGED) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + n * 512), 16, voff[k],
-                                                   so, 0, 0);
+        if (!ragged) {
+          // (through a local: handing the member element straight to the
+          // builtin made the host compilation drop the kernels' launch stubs)
+          const uint32_t vo = voff[k];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + n * 512), 16, vo, so,
+                                                   0, 0);
         } else {
           const uint32_t o =
               voff[k] != kOutOfRange && r0 + row[k] < lim ? voff[k] + so : kOutOfRange;
@@ -236,9 +237,9 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   // issues the same loads, so the load counts the waits assume hold
   auto issue = [&](bf16_t* k, bf16_t* kl, bf16_t* v, int kt) {
     const int r0 = min(kt, kt_hi) * kBKV;
-    dq_.template issue<RAGGED>(rk, k, wave, r0, S, ldq);
-    if (SPLIT) dl_.template issue<RAGGED>(rl, kl, wave, r0, S, ldl);
-    dq_.template issue<RAGGED>(rv, v, wave, r0, S, ldq);
+    dq_.issue(RAGGED, rk, k, wave, r0, S, ldq);
+    if (SPLIT) dl_.issue(RAGGED, rl, kl, wave, r0, S, ldl);
+    dq_.issue(RAGGED, rv, v, wave, r0, S, ldq);
   };
 
   bf16x8_t qf[D / 16], qf_lo[D / 16];
@@ -432,14 +433,18 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
   // tiles past qt_hi reload tile qt_hi (never used; keeps the load counts)
   auto issue = [&](bf16_t* q, bf16_t* ql, bf16_t* o, float* ls, float* dd, int qt) {
     const int i0 = min(qt, qt_hi) * kBKV;
-    dq_.template issue<RAGGED>(rq, q, wave, i0, S, ldq);
-    if (SPLIT) dl_.template issue<RAGGED>(rl, ql, wave, i0, S, ldl);
-    do_.template issue<RAGGED>(ro, o, wave, i0, S, ld_do);
+    dq_.issue(RAGGED, rq, q, wave, i0, S, ldq);
+    if (SPLIT) dl_.issue(RAGGED, rl, ql, wave, i0, S, ldl);
+    do_.issue(RAGGED, ro, o, wave, i0, S, ld_do);
     if (wave == 0) {
+      // whole tiles: fixed lane offset plus the tile's scalar offset; the
+      // ragged variant folds the tile offset into the lane offset and sends
+      // rows at or beyond S out of range
       const uint32_t so = (uint32_t)i0 * 4u;
-      const uint32_t vo = RAGGED && i0 + lane >= S ? kOutOfRange : lane4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rls, (lds_void_t*)ls, 4, vo, RAGGED ? 0 : so, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rdd, (lds_void_t*)dd, 4, vo, RAGGED ? 0 : so, 0, 0);
+      const uint32_t vo = !RAGGED ? lane4 : (i0 + lane < S ? lane4 + so : kOutOfRange);
+      const uint32_t sv = RAGGED ? 0u : so;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rls, (lds_void_t*)ls, 4, vo, sv, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rdd, (lds_void_t*)dd, 4, vo, sv, 0, 0);
     }
   };
 
@@ -588,9 +593,9 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   // issues the same loads, so the load counts the waits assume hold
   auto issue = [&](bf16_t* k, bf16_t* kl, bf16_t* v, int kt) {
     const int r0 = min(kt, kt_hi) * kBKV;
-    dq_.template issue<RAGGED>(rk, k, wave, r0, S, ldq);
-    if (SPLIT) dl_.template issue<RAGGED>(rl, kl, wave, r0, S, ldl);
-    dq_.template issue<RAGGED>(rv, v, wave, r0, S, ldq);
+    dq_.issue(RAGGED, rk, k, wave, r0, S, ldq);
+    if (SPLIT) dl_.issue(RAGGED, rl, kl, wave, r0, S, ldl);
+    dq_.issue(RAGGED, rv, v, wave, r0, S, ldq);
   };
 
   bf16x8_t qf[D / 16], of[D / 16], qf_lo[D / 16];
@@ -777,31 +782,39 @@ __global__ __launch_bounds__(128) void swa_bwd_dkdv_simt(
   for (int c = 0; c < D; ++c) { row[A + c] = dk[c] * scale; row[2 * A + c] = dv[c]; }
 }
 
-// Calls f(split, ragged) with both flags as compile-time constants.
-template <class F>
-void dispatch2(bool split, bool ragged, F&& f) {
-  using T = std::true_type;
-  using U = std::false_type;
-  if (split) {
-    if (ragged) f(T{}, T{}); else f(T{}, U{});
-  } else {
-    if (ragged) f(U{}, T{}); else f(U{}, U{});
-  }
+template <int D, bool SP, bool RG>
+void launch_fwd_mfma(const SwaDesc& a, void* o, int64_t ldo, float* lse, float scale,
+                     hipStream_t s) {
+  dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
+  const int64_t ldl = 2 * (int64_t)a.n_heads * D;
+  hipLaunchKernelGGL((swa_fwd_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
+                     (const bf16_t*)a.qkv, a.ld_qkv, (const bf16_t*)a.qk_lo, ldl, (bf16_t*)o, ldo,
+                     lse, a.seq, a.n_heads, a.window, scale * kLog2e);
+}
+
+template <int D, bool SP, bool RG>
+void launch_bwd_mfma(const SwaDesc& a, const void* d_o, int64_t ld_do, const float* lse,
+                     const float* dvec, void* dqkv, int64_t ldd, float scale, hipStream_t s) {
+  dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
+  const int64_t ldl = 2 * (int64_t)a.n_heads * D;
+  const bf16_t* lo = (const bf16_t*)a.qk_lo;
+  hipLaunchKernelGGL((swa_bwd_dkdv_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
+                     (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse, dvec,
+                     (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window, scale * kLog2e, scale);
+  hipLaunchKernelGGL((swa_bwd_dq_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
+                     (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse, dvec,
+                     (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window, scale * kLog2e, scale);
 }
 
 template <int D>
 hipError_t fwd_d(int dtype, const SwaDesc& a, void* o, int64_t ldo, float* lse, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)D);
   if (dtype == 1) {
-    dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
-    const int64_t ldl = 2 * (int64_t)a.n_heads * D;
-    auto go = [&](auto split, auto ragged) {
-      hipLaunchKernelGGL((swa_fwd_mfma<D, decltype(split)::value, decltype(ragged)::value>), grid,
-                         dim3(kSwaThreads), 0, s, (const bf16_t*)a.qkv, a.ld_qkv,
-                         (const bf16_t*)a.qk_lo, ldl, (bf16_t*)o, ldo, lse, a.seq, a.n_heads,
-                         a.window, scale * kLog2e);
-    };
-    dispatch2(a.qk_lo != nullptr, a.seq % kBKV != 0, go);
+    const bool sp = a.qk_lo != nullptr, rg = a.seq % kBKV != 0;
+    if (sp && rg) launch_fwd_mfma<D, true, true>(a, o, ldo, lse, scale, s);
+    else if (sp) launch_fwd_mfma<D, true, false>(a, o, ldo, lse, scale, s);
+    else if (rg) launch_fwd_mfma<D, false, true>(a, o, ldo, lse, scale, s);
+    else launch_fwd_mfma<D, false, false>(a, o, ldo, lse, scale, s);
   } else {
     const int64_t n = (int64_t)a.batch * a.n_heads * a.seq;
     hipLaunchKernelGGL((swa_fwd_simt<D>), dim3((n + 127) / 128), dim3(128), 0, s,
@@ -821,21 +834,12 @@ hipError_t bwd_d(int dtype, const SwaDesc& a, const void* o, int64_t ldo, const 
     hipLaunchKernelGGL((swa_rowdot<bf16_t>), dim3((n + 255) / 256), dim3(256), 0, s,
                        (const bf16_t*)d_o, ld_do, (const bf16_t*)o, ldo, dvec, a.batch, a.seq,
                        a.n_heads, D);
-    dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
-    const int64_t ldl = 2 * (int64_t)a.n_heads * D;
-    const bf16_t* lo = (const bf16_t*)a.qk_lo;
-    auto go = [&](auto split, auto ragged) {
-      constexpr bool SP = decltype(split)::value, RG = decltype(ragged)::value;
-      hipLaunchKernelGGL((swa_bwd_dkdv_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
-                         (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse,
-                         (const float*)dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window,
-                         scale * kLog2e, scale);
-      hipLaunchKernelGGL((swa_bwd_dq_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
-                         (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse,
-                         (const float*)dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window,
-                         scale * kLog2e, scale);
-    };
-    dispatch2(lo != nullptr, a.seq % kBKV != 0, go);
+    const bool sp = a.qk_lo != nullptr, rg = a.seq % kBKV != 0;
+    const float* dv = dvec;
+    if (sp && rg) launch_bwd_mfma<D, true, true>(a, d_o, ld_do, lse, dv, dqkv, ldd, scale, s);
+    else if (sp) launch_bwd_mfma<D, true, false>(a, d_o, ld_do, lse, dv, dqkv, ldd, scale, s);
+    else if (rg) launch_bwd_mfma<D, false, true>(a, d_o, ld_do, lse, dv, dqkv, ldd, scale, s);
+    else launch_bwd_mfma<D, false, false>(a, d_o, ld_do, lse, dv, dqkv, ldd, scale, s);
   } else {
     hipLaunchKernelGGL((swa_rowdot<float>), dim3((n + 255) / 256), dim3(256), 0, s,
                        (const float*)d_o, ld_do, (const float*)o, ldo, dvec, a.batch, a.seq,
