@@ -20,12 +20,13 @@
 //     the current one is multiplied); the transposed operands (V^T, dO^T,
 //     Q^T, K^T) are read from those row-major tiles with the transposing
 //     LDS read, so no transposed copy is ever staged.
-//   * backward (FlashAttention-2 style, no atomics, deterministic):
-//     D_i = dO_i . O_i; then one kernel per 128-key block accumulates dK and
-//     dV over the query tiles of the band (S = Q K^T, P = exp(S - lse),
-//     dP = dO V^T, dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS), and one
-//     kernel per 128-query block accumulates dQ^T += K^T dS^T with the
-//     transposed formulation of the forward.
+//   * backward (FlashAttention-2 style, no atomics, deterministic): one
+//     kernel per 128-query block forms D_i = dO_i . O_i for its queries
+//     (and stores it) and accumulates dQ^T += K^T dS^T with the transposed
+//     formulation of the forward; then one kernel per 128-key block
+//     accumulates dK and dV over the query tiles of the band (S = Q K^T,
+//     P = exp(S - lse), dP = dO V^T, dS = P (dP - D), dV^T += dO^T P,
+//     dK^T += Q^T dS).
 // fp32 path: one thread per query (or key) looping over its window; it serves
 // the fp32 workload only.
 #include "common.h"
@@ -353,8 +354,9 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
 }
 
 // ------------------------------------------------------------------ D = rowsum(dO * O)
-// One thread per (batch, head, query); the head's D values of dO and O move
-// as 8-element vectors (D is a multiple of 8).
+// fp32 path (the bf16 path forms D inside the dQ kernel): one thread per
+// (batch, head, query); the head's D values of dO and O move as 8-element
+// vectors (D is a multiple of 8).
 template <typename T>
 __global__ __launch_bounds__(256) void swa_rowdot(const T* __restrict__ d_o, int64_t ld_do,
                                                   const T* __restrict__ o, int64_t ldo,
@@ -554,8 +556,8 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
 template <int D, bool SPLIT, bool RAGGED>
 __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
     const bf16_t* __restrict__ qkv, int64_t ldq, const bf16_t* __restrict__ qk_lo, int64_t ldl,
-    const bf16_t* __restrict__ d_o, int64_t ld_do,
-    const float* __restrict__ lse, const float* __restrict__ dvec, bf16_t* __restrict__ dqkv,
+    const bf16_t* __restrict__ d_o, int64_t ld_do, const bf16_t* __restrict__ o, int64_t ldo,
+    const float* __restrict__ lse, float* __restrict__ dvec, bf16_t* __restrict__ dqkv,
     int64_t ldd, int S, int H, int W, float sl2, float scale) {
   constexpr int NS = kSwaStages<D>;
   constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8, T3 = NS > 2 ? TE : 8,
@@ -602,10 +604,24 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   load_row_frags<D>(qf, Qp, ldq, qi, S, lane);
   load_row_frags<D>(of, dOp, ld_do, qi, S, lane);
   if (SPLIT) load_row_frags<D>(qf_lo, lo_base + h * D, ldl, qi, S, lane);
+  // D_i = dO_i . O_i for this wave's queries: lanes l and l + 32 hold the
+  // two halves of each K=16 step of query l's row; the dK/dV kernel, launched
+  // after this one, reads the values back
+  float di;
+  {
+    bf16x8_t ofo[D / 16];
+    load_row_frags<D>(ofo, o + (int64_t)b * S * ldo + h * D, ldo, qi, S, lane);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part += bf2f(of[ks][e]) * bf2f(ofo[ks][e]);
+    di = part + __shfl_xor(part, 32, 64);
+    if (lane < 32 && qi < S) dvec[((int64_t)b * H + h) * S + qi] = di;
+  }
   issue(K0, L0, V0, kt_lo);
   if (NS > 2) issue(K1, L1, V1, kt_lo + 1);
   const float lse2 = qi < S ? lse[((int64_t)b * H + h) * S + qi] * kLog2e : 0.f;
-  const float di = qi < S ? dvec[((int64_t)b * H + h) * S + qi] : 0.f;
   f32x16_t dq[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
@@ -792,18 +808,22 @@ void launch_fwd_mfma(const SwaDesc& a, void* o, int64_t ldo, float* lse, float s
                      lse, a.seq, a.n_heads, a.window, scale * kLog2e);
 }
 
+// dQ first: it also writes D = rowsum(dO * O), which dK/dV then reads.
 template <int D, bool SP, bool RG>
-void launch_bwd_mfma(const SwaDesc& a, const void* d_o, int64_t ld_do, const float* lse,
-                     const float* dvec, void* dqkv, int64_t ldd, float scale, hipStream_t s) {
+void launch_bwd_mfma(const SwaDesc& a, const void* o, int64_t ldo, const void* d_o,
+                     int64_t ld_do, const float* lse, float* dvec, void* dqkv, int64_t ldd,
+                     float scale, hipStream_t s) {
   dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
   const int64_t ldl = 2 * (int64_t)a.n_heads * D;
   const bf16_t* lo = (const bf16_t*)a.qk_lo;
-  hipLaunchKernelGGL((swa_bwd_dkdv_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
-                     (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse, dvec,
-                     (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window, scale * kLog2e, scale);
   hipLaunchKernelGGL((swa_bwd_dq_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
-                     (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse, dvec,
-                     (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window, scale * kLog2e, scale);
+                     (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do,
+                     (const bf16_t*)o, ldo, lse, dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads,
+                     a.window, scale * kLog2e, scale);
+  hipLaunchKernelGGL((swa_bwd_dkdv_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
+                     (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do, lse,
+                     (const float*)dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads, a.window,
+                     scale * kLog2e, scale);
 }
 
 template <int D>
@@ -831,15 +851,10 @@ hipError_t bwd_d(int dtype, const SwaDesc& a, const void* o, int64_t ldo, const 
   const float scale = 1.0f / sqrtf((float)D);
   const int64_t n = (int64_t)a.batch * a.n_heads * a.seq;
   if (dtype == 1) {
-    hipLaunchKernelGGL((swa_rowdot<bf16_t>), dim3((n + 255) / 256), dim3(256), 0, s,
-                       (const bf16_t*)d_o, ld_do, (const bf16_t*)o, ldo, dvec, a.batch, a.seq,
-                       a.n_heads, D);
     const bool sp = a.qk_lo != nullptr, rg = a.seq % kBKV != 0;
-    const float* dv = dvec;
-    if (sp && rg) launch_bwd_mfma<D, true, true>(a, d_o, ld_do, lse, dv, dqkv, ldd, scale, s);
-    else if (sp) launch_bwd_mfma<D, true, false>(a, d_o, ld_do, lse, dv, dqkv, ldd, scale, s);
-    else if (rg) launch_bwd_mfma<D, false, true>(a, d_o, ld_do, lse, dv, dqkv, ldd, scale, s);
-    else launch_bwd_mfma<D, false, false>(a, d_o, ld_do, lse, dv, dqkv, ldd, scale, s);
+    auto* f = sp ? (rg ? launch_bwd_mfma<D, true, true> : launch_bwd_mfma<D, true, false>)
+                 : (rg ? launch_bwd_mfma<D, false, true> : launch_bwd_mfma<D, false, false>);
+    f(a, o, ldo, d_o, ld_do, lse, dvec, dqkv, ldd, scale, s);
   } else {
     hipLaunchKernelGGL((swa_rowdot<float>), dim3((n + 255) / 256), dim3(256), 0, s,
                        (const float*)d_o, ld_do, (const float*)o, ldo, dvec, a.batch, a.seq,
