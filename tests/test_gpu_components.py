@@ -144,6 +144,9 @@ SWA_CASES = [
     # batch, seq, heads, head_dim, window
     (1, 128, 2, 64, 32), (2, 200, 3, 96, 50), (1, 333, 2, 128, 333), (1, 260, 2, 96, 1),
     (2, 130, 1, 64, 1000), (1, 520, 2, 128, 129), (1, 64, 1, 96, 64), (1, 1, 1, 64, 5),
+    # whole 64-row tiles, several tiles per band (the three-stage tile ring
+    # for d <= 96, the two-stage one for d = 128)
+    (2, 512, 2, 96, 200), (1, 448, 1, 64, 448), (1, 384, 2, 128, 150),
 ]
 
 
