@@ -24,7 +24,9 @@
  *   - Device pointers must be 16-byte aligned.
  *   - Matrices are row-major.  Activations are token-major [T, width] with
  *     T = batch * seq and the tokens of one sequence contiguous.
- *   - Calls are reentrant; the library keeps no mutable global state.
+ *   - Calls are reentrant.  The only mutable global state is an atomic
+ *     per-process launch counter that tags the split-K arrival counters in
+ *     the GEMM workspace (so workspace contents never need initialising).
  */
 #ifndef PTB_H
 #define PTB_H
@@ -80,12 +82,12 @@ typedef struct {
 /* Bytes of the `saved` buffer that ptb_forward fills and ptb_backward reads
  * (LN output and statistics, Q|K|V, FC1 pre-activation, [O | GeLU(FC1)],
  * attention log-sum-exp; for bf16 also the rounding residuals of the LN
- * output and of q, k, and a 128 MiB tail that the forward GEMMs use as
- * workspace for split-K partial tiles).  0 if dims are invalid. */
+ * output and of q, k, and a 128 MiB + 32 KiB tail that the forward GEMMs
+ * use as workspace for split-K partial tiles and their arrival counters).  0 if dims are invalid. */
 size_t ptb_saved_bytes(const ptb_dims* dims);
 
 /* Bytes of the temporary `scratch` buffer ptb_backward needs (bf16: including
- * 128 MiB of GEMM split-K workspace).  0 if invalid. */
+ * 128 MiB + 32 KiB of GEMM split-K workspace).  0 if invalid. */
 size_t ptb_scratch_bytes(const ptb_dims* dims);
 
 /* Forward of one shard ([MS] PTB and SWA rows):
@@ -117,7 +119,7 @@ int ptb_backward(const ptb_dims* dims, const void* x, const float* ln_gamma,
  * tensor-parallel shard this computes the shard's weights as a whole layer.
  * Buffers and errors as for ptb_forward / ptb_backward; sizes from
  * ptb_serial_saved_bytes / ptb_serial_scratch_bytes (bf16: each includes a
- * 128 MiB GEMM workspace tail).  Backward overwrites dx, the four LN
+ * 128 MiB + 32 KiB GEMM workspace tail).  Backward overwrites dx, the four LN
  * gradients (fp32), dw_in and dw_out. */
 size_t ptb_serial_saved_bytes(const ptb_dims* dims);
 size_t ptb_serial_scratch_bytes(const ptb_dims* dims);

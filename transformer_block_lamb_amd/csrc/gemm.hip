@@ -28,6 +28,9 @@
 //
 // fp32 path: a plain LDS-tiled SIMT kernel (64x64 tile, 4x4 outputs per
 // thread) with the same epilogues; it serves the fp32 workload.
+#include <atomic>
+#include <chrono>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -411,8 +414,10 @@ struct Sched {
 // are split into `grid` equal contiguous ranges (stream-K), so every CU gets
 // the same amount of work when the tile count is not a multiple of the CU
 // count.  A range that covers only part of a tile writes its fp32 partial
-// tile to ws; a second kernel sums the partials of each split tile in K
-// order and runs the epilogue, so results do not depend on timing.
+// tile to ws and counts itself in the tile's arrival counter; the workgroup
+// that completes the count sums the tile's partials from ws in K order and
+// runs the epilogue, so results do not depend on timing or on which
+// contributor finishes last.
 struct GemmArgs {
   const bf16_t* a;
   const bf16_t* b;
@@ -425,10 +430,15 @@ struct GemmArgs {
   int sk, grid, dp_tiles;
   int64_t sk_base, sk_iters;
   float* ws;
+  unsigned long long* arrive;  // one counter per split tile (logical tile - dp_tiles)
+  unsigned long long tag;      // 48-bit launch tag
   int use_perm;
   int16_t perm[kMaxPerm];  // N-tile order (when use_perm, sk == 0)
 };
 constexpr int kPartialFloats = BM * BN;  // one partial tile in ws
+// Cache policy of the partial-tile accesses: device scope (sc1), coherent
+// across the XCDs' L2s.
+constexpr int kCpolDevice = 16;
 
 // First iteration of stream-K worker w (w == grid: end of the range);
 // rounded down to a multiple of kSkAlign.
@@ -448,6 +458,31 @@ __device__ inline int sk_owner(const GemmArgs& g, int64_t it) {
 // segment (which may start inside the tile) or its last one.
 __device__ inline int sk_slot(const GemmArgs& g, int w, int64_t s) {
   return sk_lo(g, w) >= s ? 2 * w : 2 * w + 1;
+}
+
+// Counts one contribution to a split tile and returns true for the one that
+// completes it (n contributions in all).  Counter word: launch tag in bits
+// 63..16, contributions so far in bits 15..0; a word carrying another tag
+// (an earlier launch, or memory never used as a counter) counts as none.
+// The completing contribution stores 0, so the counters also stay valid
+// when a captured launch is replayed with the same tag.  Every failed
+// exchange means another contributor's exchange succeeded, so the loop ends
+// after at most n rounds; the bound only guards against foreign writes.
+// The exchange itself is device-scope and relaxed: the partials it guards
+// are written and read with device-scope (sc1) accesses, the writer waits
+// for its stores to complete before counting, and the reader loads only
+// after the verdict, so no cache-wide release or acquire is needed.
+__device__ __forceinline__ bool arrive_last(unsigned long long* c, unsigned long long tag, int n) {
+  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int tries = 0; tries < 4096; ++tries) {
+    const unsigned long long have = (old >> 16) == tag ? (old & 0xffffull) : 0ull;
+    const bool last = (int)have + 1 >= n;
+    const unsigned long long next = last ? 0ull : (tag << 16) | (have + 1);
+    if (__hip_atomic_compare_exchange_strong(c, &old, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return last;
+  }
+  return false;
 }
 
 // 8 MFMAs of one K=16 step: the wave's 128x64 accumulators.
@@ -579,7 +614,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   const int64_t it_end = g.sk ? sk_lo(g, gl + 1) : 0;
   bool first_sk = true;
   for (;;) {
-    int tm, tn, kb, ke, slot = -1;
+    int tm, tn, kb, ke, slot = -1, lt = 0;
     if (dp_left > 0) {
       if (g.sk) {
         g.sc.tile(dp_next, tm, tn);
@@ -591,9 +626,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       kb = 0;
       ke = g.sc.cost(tn);
     } else if (it < it_end) {
-      int l, koff;
-      g.sc.locate(it, l, koff);
-      g.sc.tile(l, tm, tn);
+      int koff;
+      g.sc.locate(it, lt, koff);
+      g.sc.tile(lt, tm, tn);
       const int c = g.sc.cost(tn);
       const int seg = (int)(it_end - it < (int64_t)(c - koff) ? it_end - it : (int64_t)(c - koff));
       kb = koff;
@@ -687,70 +722,68 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       for (int i = 0; i < 4; ++i)
         epilogue_strip(acc[i], stage, m0 + wm * 128 + i * 32, n0 + wn * 64, lane, g.M, g.N, epi);
     } else {
-      float* p = g.ws + (size_t)slot * kPartialFloats;
+      // Partials move with device-scope (sc1) buffer stores and loads, which
+      // other XCDs see without a writeback or invalidation of the whole L2.
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.ws, (uint32_t)kGemmPartialBytes);
+      const uint32_t so =
+          __builtin_amdgcn_readfirstlane((uint32_t)slot * (uint32_t)(kPartialFloats * 4));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            *reinterpret_cast<float4*>(p + partial_off(wave, i, j, r4, lane)) =
-                make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
-                            acc[i][j][4 * r4 + 3]);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4_t v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                               acc[i][j][4 * r4 + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rw, (uint32_t)partial_off(wave, i, j, r4, lane) * 4,
+                                                   so, kCpolDevice);
+          }
+      // Count the partial once every wave's stores have completed.  Every
+      // LDS slot is idle here (the loads were drained above and the next
+      // segment's first loads come after a barrier), so slot s4 carries the
+      // verdict to the workgroup.
+      const int64_t ts = g.sc.start(lt), te = g.sc.start(lt + 1);
+      const int w0 = sk_owner(g, ts), w1 = sk_owner(g, te - 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      int* verdict = reinterpret_cast<int*>(s4);
+      if (threadIdx.x == 0) {
+        int n = 0;
+        for (int w = w0; w <= w1; ++w) n += sk_lo(g, w) != sk_lo(g, w + 1);
+        *verdict = arrive_last(g.arrive + (lt - g.dp_tiles), g.tag, n) ? 1 : 0;
+      }
+      __syncthreads();
+      if (*verdict != 0) {
+        // The tile is complete: add its partials in worker (= K) order (this
+        // workgroup's own read back like the others, so the accumulators are
+        // free) and run the epilogue.
+#pragma unroll 1
+        for (int i = 0; i < 4; ++i) {
+          f32x16_t a[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[j][r] = 0.f;
+#pragma unroll 1
+          for (int w = w0; w <= w1; ++w) {
+            if (sk_lo(g, w) == sk_lo(g, w + 1)) continue;
+            const uint32_t src = __builtin_amdgcn_readfirstlane(
+                (uint32_t)sk_slot(g, w, ts) * (uint32_t)(kPartialFloats * 4));
+            f32x4_t v[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+              v[c] = __builtin_amdgcn_raw_buffer_load_b128(
+                  rw, (uint32_t)partial_off(wave, i, c >> 2, c & 3, lane) * 4, src, kCpolDevice);
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) a[c >> 2][4 * (c & 3) + e] += v[c][e];
+          }
+          epilogue_strip(a, stage, m0 + wm * 128 + i * 32, n0 + wn * 64, lane, g.M, g.N, epi);
+        }
+      }
     }
   }
-}
-
-// Stream-K fixup: one workgroup per 64-row strip (accumulator row i) of each
-// tile of the split part; a tile whose iterations several workers shared
-// gets the sum of their partials, added in worker (= K) order, and the
-// epilogue.  Two partials at a time are loaded before either is added, so
-// their loads are in flight together.
-template <class Epi>
-__global__ __launch_bounds__(kGemmThreads) void gemm_fixup_kernel(GemmArgs g, Epi epi) {
-  __shared__ __attribute__((aligned(16))) float stage_all[kWaves][2 * kStageBlk];
-  const int l = g.dp_tiles + (blockIdx.x >> 2), i = blockIdx.x & 3;
-  const int64_t s = g.sc.start(l), e = g.sc.start(l + 1);
-  const int w0 = sk_owner(g, s), w1 = sk_owner(g, e - 1);
-  if (w0 == w1) return;  // one worker computed the whole tile
-  int tm, tn;
-  g.sc.tile(l, tm, tn);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
-  f32x16_t a[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) a[j][r] = 0.f;
-#pragma unroll 1
-  for (int w = w0; w <= w1;) {
-    // the next (up to) two non-empty contributors, in order
-    const float* src[2];
-    int n = 0;
-    for (; w <= w1 && n < 2; ++w)
-      if (sk_lo(g, w) != sk_lo(g, w + 1)) src[n++] = g.ws + (size_t)sk_slot(g, w, s) * kPartialFloats;
-    float4 v[2][8];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (q < n)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          v[q][c] = *reinterpret_cast<const float4*>(src[q] + partial_off(wave, i, c >> 2, c & 3, lane));
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (q < n)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          f32x16_t& t = a[c >> 2];
-          const int r = 4 * (c & 3);
-          t[r] += v[q][c].x;
-          t[r + 1] += v[q][c].y;
-          t[r + 2] += v[q][c].z;
-          t[r + 3] += v[q][c].w;
-        }
-  }
-  epilogue_strip(a, stage_all[wave], tm * BM + wm * 128 + i * 32, tn * BN + wn * 64, lane, g.M,
-                 g.N, epi);
 }
 
 // --------------------------------------------------------------- fp32 SIMT
@@ -829,6 +862,15 @@ int persistent_grid() {
   return cached[dev] > 0 ? cached[dev] : 0;
 }
 
+// A 48-bit tag per split launch, so arrival counters left by earlier
+// launches (or never initialised) read as empty.  Starts at a clock-derived
+// value so that a fresh process does not reuse the tags of an earlier one.
+unsigned long long next_launch_tag() {
+  static std::atomic<unsigned long long> counter{
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull};
+  return counter.fetch_add(1, std::memory_order_relaxed) & 0xffffffffffffull;
+}
+
 template <int AL, int BL, class Epi>
 hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
   GemmArgs g;
@@ -853,6 +895,8 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
   g.grid = 8;
   g.dp_tiles = 0;
   g.sk_base = g.sk_iters = 0;
+  g.arrive = nullptr;
+  g.tag = 0;
 
   // Stream-K when whole tiles per CU would leave more than a tenth of the
   // machine idle: compare the ideal share of K iterations per CU with the
@@ -889,6 +933,16 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
       }
       g.sk_base = g.sc.start(g.dp_tiles);
       g.sk_iters = total - g.sk_base;
+      if (tiles - g.dp_tiles > kSkMaxSplitTiles) {
+        g.sk = 0;  // more split tiles than arrival counters
+        g.sc = Sched{ntm, ntn, (d.K + BK - 1) / BK, nh, kGroupM, 0};
+        g.grid = 8;
+        g.dp_tiles = 0;
+        g.sk_base = g.sk_iters = 0;
+      } else {
+        g.arrive = reinterpret_cast<unsigned long long*>(static_cast<char*>(d.ws) + kGemmPartialBytes);
+        g.tag = next_launch_tag();
+      }
     }
   }
   if (!g.sk) {
@@ -919,10 +973,6 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<AL, BL, true, Epi>), dim3(g.grid), dim3(kGemmThreads), 0,
                        s, g, epi);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gemm_fixup_kernel<Epi>), dim3(4 * (tiles - g.dp_tiles)), dim3(kGemmThreads), 0,
-                     s, g, epi);
   return hipGetLastError();
 }
 

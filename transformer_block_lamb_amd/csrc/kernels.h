@@ -28,9 +28,12 @@ struct GemmDesc {
   size_t ws_bytes = 0;
 };
 // Stream-K: at most kSkMaxGrid persistent workgroups, each with two fp32
-// 256 x 256 partial tiles in the workspace.
+// 256 x 256 partial tiles in the workspace, followed by one 8-byte arrival
+// counter per split tile (at most kSkMaxSplitTiles).
 constexpr int kSkMaxGrid = 256;
-constexpr size_t kGemmWsBytes = (size_t)2 * kSkMaxGrid * 256 * 256 * 4;
+constexpr int kSkMaxSplitTiles = 4096;
+constexpr size_t kGemmPartialBytes = (size_t)2 * kSkMaxGrid * 256 * 256 * 4;
+constexpr size_t kGemmWsBytes = kGemmPartialBytes + (size_t)kSkMaxSplitTiles * 8;
 
 // ---- layernorm.hip
 // xn_lo (bf16 only, may be null): receives xn - bf16(xn) rounded to bf16.
