@@ -32,7 +32,7 @@ enum {
   PTB_BWD_GEMM_DW_OUT = 1, /* dw_out = cat^T dy                                 */
   PTB_BWD_ATTENTION = 2,   /* D = rowsum(dO O); dK, dV; dQ -> dz[:, :3A]        */
   PTB_BWD_GEMM_DW_IN = 3,  /* dw_in = dz^T xn                                   */
-  PTB_BWD_GEMM_DXN = 4,    /* dxn = dz w_in (fp32 temporary)                    */
+  PTB_BWD_GEMM_DXN = 4,    /* dxn = dz w_in (temporary in the layer dtype)      */
   PTB_BWD_LAYERNORM = 5,   /* dx = LN'(dxn) [+ dy]; dgamma, dbeta               */
   PTB_BWD_STAGES = 6
 };

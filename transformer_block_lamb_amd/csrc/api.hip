@@ -84,7 +84,7 @@ struct ScratchLayout {
     size_t o = 0;
     d_o = o;   o += up(d.T * d.A * d.e);
     dz = o;    o += up(d.T * d.N1 * d.e);
-    dxn = o;   o += up(d.T * d.h * 4);
+    dxn = o;   o += up(d.T * d.h * d.e);
     dvec = o;  o += up(d.B * d.H * d.S * 4);
     gpart = o; o += up(nblk * d.h * 4);
     bpart = o; o += up(nblk * d.h * 4);
@@ -223,7 +223,7 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
   const float* lse = at<float>(saved, L.lse);
   void* d_o = at<char>(scratch, R.d_o);
   void* dz = at<char>(scratch, R.dz);
-  float* dxn = at<float>(scratch, R.dxn);
+  void* dxn = at<char>(scratch, R.dxn);
   float* dvec = at<float>(scratch, R.dvec);
   float* gpart = at<float>(scratch, R.gpart);
   float* bpart = at<float>(scratch, R.bpart);
@@ -258,11 +258,11 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
         e = launch_gemm_store(dt, g, dw_in, d.h, false, stream);
         break;
       }
-      case PTB_BWD_GEMM_DXN: {  // dxn = dz w_in (fp32)
+      case PTB_BWD_GEMM_DXN: {  // dxn = dz w_in
         GemmDesc g{(int)d.T, (int)d.h, (int)d.N1, kKContig, kMNContig, dz, d.N1, w_in, d.h};
         g.ws = ws;
         g.ws_bytes = ws_bytes;
-        e = launch_gemm_store(dt, g, dxn, d.h, true, stream);
+        e = launch_gemm_store(dt, g, dxn, d.h, false, stream);
         break;
       }
       case PTB_BWD_LAYERNORM: {  // dx (+ dy), then the deterministic dgamma/dbeta reduce
@@ -324,7 +324,7 @@ struct SerialScratchLayout {
     size_t o = 0;
     d_o = o;   o += up(d.T * d.A * d.e);
     dz = o;    o += up(d.T * d.N1 * d.e);
-    dxn = o;   o += up(d.T * d.h * 4);
+    dxn = o;   o += up(d.T * d.h * d.e);
     dh = o;    o += up(d.T * d.h * d.e);
     dvec = o;  o += up(d.B * d.H * d.S * 4);
     gpart = o; o += up(nblk * d.h * 4);
@@ -446,7 +446,7 @@ int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_ga
   const void* f = at<char>(saved, L.f);
   void* d_o = at<char>(scratch, R.d_o);
   void* dz = at<char>(scratch, R.dz);
-  float* dxn = at<float>(scratch, R.dxn);
+  void* dxn = at<char>(scratch, R.dxn);
   void* dh = at<char>(scratch, R.dh);
   float* gpart = at<float>(scratch, R.gpart);
   float* bpart = at<float>(scratch, R.bpart);
@@ -476,10 +476,10 @@ int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_ga
     e = launch_gemm_store(dt, gemm((int)d.F, (int)d.h, (int)d.T, kMNContig, kMNContig,
                                    off(dz, 3 * d.A, d.e), d.N1, xn2, d.h),
                           dw_in_c + 3 * d.A * d.h * d.e, d.h, false, stream);
-  if (e == hipSuccess)  // dxn2 = df w_fc1 (fp32)
+  if (e == hipSuccess)  // dxn2 = df w_fc1
     e = launch_gemm_store(dt, gemm((int)d.T, (int)d.h, (int)d.F, kKContig, kMNContig,
                                    off(dz, 3 * d.A, d.e), d.N1, off(w_in, 3 * d.A * d.h, d.e), d.h),
-                          dxn, d.h, true, stream);
+                          dxn, d.h, false, stream);
   if (e == hipSuccess)  // dh = dy + LN2 backward
     e = launch_ln_bwd(dt, hid, ln2_gamma, at<float>(saved, L.mean2), at<float>(saved, L.rstd2),
                       dxn, dy, dh, gpart, bpart, (int)d.T, (int)d.h, stream);
@@ -501,10 +501,10 @@ int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_ga
     e = launch_gemm_store(dt, gemm((int)(3 * d.A), (int)d.h, (int)d.T, kMNContig, kMNContig, dz,
                                    d.N1, xn1, d.h),
                           dw_in, d.h, false, stream);
-  if (e == hipSuccess)  // dxn1 = dqkv w_qkv (fp32)
+  if (e == hipSuccess)  // dxn1 = dqkv w_qkv
     e = launch_gemm_store(dt, gemm((int)d.T, (int)d.h, (int)(3 * d.A), kKContig, kMNContig, dz,
                                    d.N1, w_in, d.h),
-                          dxn, d.h, true, stream);
+                          dxn, d.h, false, stream);
   if (e == hipSuccess)  // dx = dh + LN1 backward
     e = launch_ln_bwd(dt, x, ln1_gamma, at<float>(saved, L.mean1), at<float>(saved, L.rstd1), dxn,
                       dh, dx, gpart, bpart, (int)d.T, (int)d.h, stream);

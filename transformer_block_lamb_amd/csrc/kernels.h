@@ -41,8 +41,9 @@ hipError_t launch_ln_fwd(int dtype, const void* x, const float* gamma, const flo
                          float eps, int rows, int width, void* xn, void* xn_lo, float* mean,
                          float* rstd, hipStream_t s);
 int ln_bwd_rows_per_block();
+// dxn in the activation dtype.
 hipError_t launch_ln_bwd(int dtype, const void* x, const float* gamma, const float* mean,
-                         const float* rstd, const float* dxn, const void* dy_residual, void* dx,
+                         const float* rstd, const void* dxn, const void* dy_residual, void* dx,
                          float* gpart, float* bpart, int rows, int width, hipStream_t s);
 hipError_t launch_ln_bwd_reduce(const float* gpart, const float* bpart, int nblk, int width,
                                 float* dgamma, float* dbeta, hipStream_t s);

@@ -8,7 +8,8 @@
 // activation dtype and the row's mean and 1/sqrt(var + eps) in fp32.  For
 // bf16, the rounding residual xn - bf16(xn) can be written too (xn_lo).
 //
-// Backward: one workgroup per ROWS_PER_BLOCK consecutive rows.  For each row
+// Backward: one workgroup per ROWS_PER_BLOCK consecutive rows; dxn comes in
+// the activation dtype (bf16 for bf16 runs).  For each row
 //   xhat = (x - mean) * rstd, dxhat = dxn * gamma,
 //   dx = rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)) [+ dy]
 // and each thread accumulates its columns' dgamma = sum dxn * xhat and
@@ -83,7 +84,7 @@ __device__ __forceinline__ void load_raw(const T* r, int nvec, Raw8<T> (&v)[NV])
 template <typename T, int NV>
 __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(
     const T* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ mean,
-    const float* __restrict__ rstd, const float* __restrict__ dxn, const T* __restrict__ dy,
+    const float* __restrict__ rstd, const T* __restrict__ dxn, const T* __restrict__ dy,
     T* __restrict__ dx, float* __restrict__ gpart, float* __restrict__ bpart, int rows,
     int width) {
   __shared__ float red[kLnWaves];
@@ -98,16 +99,16 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) { ag[i][e] = 0.f; ab[i][e] = 0.f; }
   Raw8<T> xr[NV], yr[NV], nxr[NV], nyr[NV];
-  Raw8<float> dr[NV], ndr[NV];
+  Raw8<T> dr[NV], ndr[NV];
   if (r0 < rend) {
     load_raw<T, NV>(x + (int64_t)r0 * width, nvec, xr);
-    load_raw<float, NV>(dxn + (int64_t)r0 * width, nvec, dr);
+    load_raw<T, NV>(dxn + (int64_t)r0 * width, nvec, dr);
     if (dy != nullptr) load_raw<T, NV>(dy + (int64_t)r0 * width, nvec, yr);
   }
   for (int row = r0; row < rend; ++row) {  // uniform over the block
     if (row + 1 < rend) {
       load_raw<T, NV>(x + (int64_t)(row + 1) * width, nvec, nxr);
-      load_raw<float, NV>(dxn + (int64_t)(row + 1) * width, nvec, ndr);
+      load_raw<T, NV>(dxn + (int64_t)(row + 1) * width, nvec, ndr);
       if (dy != nullptr) load_raw<T, NV>(dy + (int64_t)(row + 1) * width, nvec, nyr);
     }
     const float mu = mean[row], rs = rstd[row];
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict_
 template <typename T, int NV>
 __global__ __launch_bounds__(kLnThreads) void ln_bwd_plain_kernel(
     const T* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ mean,
-    const float* __restrict__ rstd, const float* __restrict__ dxn, const T* __restrict__ dy,
+    const float* __restrict__ rstd, const T* __restrict__ dxn, const T* __restrict__ dy,
     T* __restrict__ dx, float* __restrict__ gpart, float* __restrict__ bpart, int rows,
     int width) {
   __shared__ float red[kLnWaves];
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_plain_kernel(
       if (vi < nvec) {
         float xv[8], dv[8];
         Vec8<T>::load(x + (int64_t)row * width + vi * 8, xv);
-        Vec8<float>::load(dxn + (int64_t)row * width + vi * 8, dv);
+        Vec8<T>::load(dxn + (int64_t)row * width + vi * 8, dv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           xh[i][e] = (xv[e] - mu) * rs;
@@ -370,25 +371,27 @@ hipError_t fwd_t(const void* x, const float* g, const float* b, float eps, int r
 
 template <typename T, int NV>
 hipError_t bwd_nv(const void* x, const float* gamma, const float* mean, const float* rstd,
-                  const float* dxn, const void* dy, void* dx, float* gp, float* bp, int rows,
+                  const void* dxn, const void* dy, void* dx, float* gp, float* bp, int rows,
                   int width, hipStream_t s) {
   const int nblk = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   // the prefetched row fits in registers up to 3 vectors per thread for
   // bf16 rows, 2 for fp32 rows
   if constexpr (NV <= (sizeof(T) == 2 ? 3 : 2))
     hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(nblk), dim3(kLnThreads), 0, s,
-                       (const T*)x, gamma, mean, rstd, dxn, (const T*)dy, (T*)dx, gp, bp, rows,
+                       (const T*)x, gamma, mean, rstd, (const T*)dxn, (const T*)dy, (T*)dx, gp, bp,
+                       rows,
                        width);
   else
     hipLaunchKernelGGL((ln_bwd_plain_kernel<T, NV>), dim3(nblk), dim3(kLnThreads), 0, s,
-                       (const T*)x, gamma, mean, rstd, dxn, (const T*)dy, (T*)dx, gp, bp, rows,
+                       (const T*)x, gamma, mean, rstd, (const T*)dxn, (const T*)dy, (T*)dx, gp, bp,
+                       rows,
                        width);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t bwd_t(const void* x, const float* gamma, const float* mean, const float* rstd,
-                 const float* dxn, const void* dy, void* dx, float* gp, float* bp, int rows,
+                 const void* dxn, const void* dy, void* dx, float* gp, float* bp, int rows,
                  int width, hipStream_t s) {
   const int nv = (width / 8 + kLnThreads - 1) / kLnThreads;
   switch (nv) {
@@ -416,7 +419,7 @@ hipError_t launch_ln_fwd(int dtype, const void* x, const float* gamma, const flo
 }
 
 hipError_t launch_ln_bwd(int dtype, const void* x, const float* gamma, const float* mean,
-                         const float* rstd, const float* dxn, const void* dy, void* dx,
+                         const float* rstd, const void* dxn, const void* dy, void* dx,
                          float* gpart, float* bpart, int rows, int width, hipStream_t s) {
   if (dtype == 1)
     return bwd_t<bf16_t>(x, gamma, mean, rstd, dxn, dy, dx, gpart, bpart, rows, width, s);
