@@ -118,6 +118,42 @@ def test_gemm_split_schedule(a_layout, b_layout, M, N, K):
         check(f"C(c_f32={c_f32}, split)", _host(outs[0]), ref, "bf16")
 
 
+def test_gemm_split_graph_replay():
+    """A split-schedule GEMM captured in a graph replays correctly.  The
+    launch tag of its split-tile arrival counters is fixed at capture; each
+    launch leaves the counters at zero, so replays, and eager launches on the
+    same workspace between them, still count from zero."""
+    M, N, K = SPLIT_SHAPES[1]
+    print(f"gemm split graph replay M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(7)
+    code, tdt = _dt("bf16")
+    a = to_device(_rand(rng, (M, K), "bf16"), tdt)
+    b = to_device(_rand(rng, (N, K), "bf16"), tdt)
+    b2 = to_device(_rand(rng, (N, K), "bf16"), tdt)
+    ws = torch.empty(B.ptb_gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    eager = torch.empty((M, N), dtype=tdt, device="cuda")
+    B.ptb_gemm(code, 0, 0, M, N, K, a, K, b, K, eager, N, 0, workspace=ws)
+    other = torch.empty_like(eager)
+    B.ptb_gemm(code, 0, 0, M, N, K, a, K, b2, K, other, N, 0, workspace=ws)
+    torch.cuda.synchronize()
+    other_ref = other.clone()
+    c = torch.empty_like(eager)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.ptb_gemm(code, 0, 0, M, N, K, a, K, b, K, c, N, 0, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        c.zero_()
+        if rep % 2:  # an eager split launch on the same workspace in between
+            other.zero_()
+            B.ptb_gemm(code, 0, 0, M, N, K, a, K, b2, K, other, N, 0, workspace=ws)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c, eager), f"replay {rep} differs from the eager result"
+        assert torch.equal(other, other_ref), f"eager launch after replay {rep} differs"
+
+
 def _swa_case(dtype, batch, seq, H, d, w):
     rng = np.random.default_rng(batch * 1000 + seq + w + d)
     A = H * d

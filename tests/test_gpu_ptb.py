@@ -25,6 +25,9 @@ RAGGED = [
     # (1000 tokens, K = 1000 not a multiple of the 64-wide K tile)
     PtbConfig("sk_lf_ragged", 1, 1800, 1024, 3, 128, 7096, 300, "bf16", 1),
     PtbConfig("sk_pure_ragged", 1, 1000, 1000, 3, 128, 8000, 100, "bf16", 1),
+    # the same light-first schedule with a 2560-wide input (40 K tiles), so
+    # each two-pass tile splits across about three workers
+    PtbConfig("sk_lf_k2560", 1, 1800, 2560, 3, 128, 7096, 300, "bf16", 1),
 ]
 
 
