@@ -5,9 +5,12 @@ block with sliding-window attention, on one MI355X:
     ptb_forward + ptb_backward + lamb_step (over the shard's six parameter
     tensors, refreshing the bf16 weights the next forward reads)
 
-timed with HIP events on the stream the library launches on.  The forward
-and backward run as their stage entry points (exactly what ptb_forward /
-ptb_backward execute) so that every kernel stage gets its own events.
+timed with HIP events on the stream the library launches on.  The timed
+steps call ptb_forward / ptb_backward / lamb_step whole, with events only at
+their boundaries; a second set of K forward + backward passes goes through
+the stage entry points (exactly what the whole calls execute) with an event
+before each stage, which gives the per-stage times and the dominant kernel's
+launch time for the roofline.
 
 Prints ONE JSON line.  `value` is the block's model TFLOP/s, 6 * N * T FLOP
 (N = matrix parameters of the shard, T = tokens; the 6N-per-token estimate of
@@ -246,41 +249,59 @@ def main():
     names = [f"fwd.{n}" for n in B.FWD_STAGES] + [f"bwd.{n}" for n in B.BWD_STAGES] + ["lamb"]
 
     def step(it, events=None):
-        k = 0
-        for s in range(len(B.FWD_STAGES)):
-            if events is not None:
-                events[k].record(); k += 1
-            shard.forward_stage(s)
-        for s in range(len(B.BWD_STAGES)):
-            if events is not None:
-                events[k].record(); k += 1
-            shard.backward_stage(s)
+        """One training step through the library's whole calls."""
         if events is not None:
-            events[k].record(); k += 1
+            events[0].record()
+        shard.forward()
+        if events is not None:
+            events[1].record()
+        shard.backward()
+        if events is not None:
+            events[2].record()
         B.lamb_step(desc, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], it, ratios, lscratch)
         if events is not None:
-            events[k].record()
+            events[3].record()
+
+    def staged(events):
+        """The same forward and backward through the stage entry points, with
+        an event before each stage (the per-stage breakdown)."""
+        k = 0
+        for s in range(len(B.FWD_STAGES)):
+            events[k].record(); k += 1
+            shard.forward_stage(s)
+        for s in range(len(B.BWD_STAGES)):
+            events[k].record(); k += 1
+            shard.backward_stage(s)
+        events[k].record()
 
     for it in range(1, args.warmup + 1):
         step(it)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
+    # the timed region: K whole steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_wall = time.perf_counter()
     for k in range(args.steps):
         step(args.warmup + 1 + k, ev[k])
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    lamb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    step_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    fb_each = [e[0].elapsed_time(e[2]) for e in ev]
 
-    per_stage = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
-                 for i, n in enumerate(names)}
-    step_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)]))
+    # per-stage breakdown: K more forward + backward passes through the
+    # stage entry points (the events between stages add about 1.5 us each,
+    # so these stages sum to slightly more than fwd_ms + bwd_ms)
     nfb = len(B.FWD_STAGES) + len(B.BWD_STAGES)
-    fb_each = [ev[k][0].elapsed_time(ev[k][nfb]) for k in range(args.steps)]
-    fwd_ms = sum(v for n, v in per_stage.items() if n.startswith("fwd."))
-    bwd_ms = sum(v for n, v in per_stage.items() if n.startswith("bwd."))
-    lamb_ms = per_stage["lamb"]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(nfb + 1)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        staged(sev[k])
+    torch.cuda.synchronize()
+    per_stage = {n: float(np.mean([sev[k][i].elapsed_time(sev[k][i + 1]) for k in range(args.steps)]))
+                 for i, n in enumerate(names[:nfb])}
+    per_stage["lamb"] = lamb_ms
 
     serial = None
     if not args.no_serial:
