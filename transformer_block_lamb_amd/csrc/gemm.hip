@@ -47,8 +47,12 @@ constexpr int kGroupM = 8;
 
 // --------------------------------------------------------------- epilogues
 // Each epilogue takes one accumulator value (operator(), used by the fp32
-// kernel) or 8 consecutive columns of one row (store8, used by the MFMA
-// kernel after staging through LDS; col % 8 == 0, columns >= ncols dropped).
+// kernel) or 8 consecutive columns of one row (used by the MFMA kernel after
+// staging through LDS; col % 8 == 0, columns >= ncols dropped) in two steps:
+// pre8 loads whatever else the columns need (the residual, the FC1
+// pre-activation) into a Pre, and store8p combines and stores.  Splitting
+// them lets a lane issue the loads of all its chunks before it waits for
+// any.
 template <typename T>
 __device__ __forceinline__ void put8(T* p, const float (&v)[8], int valid) {
   if (valid >= 8) {
@@ -66,6 +70,45 @@ __device__ __forceinline__ void get8(const T* p, float (&v)[8], int valid) {
   }
 }
 
+// Eight values of an epilogue operand as loaded (bf16 stays packed until it
+// is used); chunks cut by the matrix edge are read at use instead.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p, int valid) {
+    if (valid >= 8) u = *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ __forceinline__ void get(const bf16_t* p, float (&v)[8], int valid) const {
+    if (valid >= 8) {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+      get8(p, v, valid);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p, int valid) {
+    if (valid >= 8) {
+      a = *reinterpret_cast<const float4*>(p);
+      b = *reinterpret_cast<const float4*>(p + 4);
+    }
+  }
+  __device__ __forceinline__ void get(const float* p, float (&v)[8], int valid) const {
+    if (valid >= 8) {
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      get8(p, v, valid);
+    }
+  }
+};
+
 template <typename T>
 struct EpiStore {
   T* c;
@@ -75,6 +118,12 @@ struct EpiStore {
   }
   __device__ __forceinline__ void store8(int row, int col, const float (&v)[8], int ncols) const {
     put8(c + (int64_t)row * ldc + col, v, ncols - col);
+  }
+  struct Pre {};
+  __device__ __forceinline__ void pre8(int, int, Pre&, int) const {}
+  __device__ __forceinline__ void store8p(int row, int col, const float (&v)[8], const Pre&,
+                                          int ncols) const {
+    store8(row, col, v, ncols);
   }
 };
 
@@ -116,6 +165,12 @@ struct EpiInFwd {
       put8(cat + (int64_t)row * (attn + ffn) + attn + c, g, valid);
     }
   }
+  struct Pre {};
+  __device__ __forceinline__ void pre8(int, int, Pre&, int) const {}
+  __device__ __forceinline__ void store8p(int row, int col, const float (&v)[8], const Pre&,
+                                          int ncols) const {
+    store8(row, col, v, ncols);
+  }
 };
 
 template <typename T>
@@ -129,19 +184,23 @@ struct EpiOutFwd {
     if (add) v += Elt<T>::ld(x + o);
     Elt<T>::st(y + o, v);
   }
-  __device__ __forceinline__ void store8(int row, int col, const float (&v)[8], int ncols) const {
+  using Pre = Raw8<T>;
+  __device__ __forceinline__ void pre8(int row, int col, Pre& p, int ncols) const {
+    if (add) p.load(x + (int64_t)row * ld + col, ncols - col);
+  }
+  __device__ __forceinline__ void store8p(int row, int col, const float (&v)[8], const Pre& p,
+                                          int ncols) const {
     const int64_t o = (int64_t)row * ld + col;
-    const int valid = ncols - col;
     float r[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = v[e];
     if (add) {
       float xv[8];
-      get8(x + o, xv, valid);
+      p.get(x + o, xv, ncols - col);
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] += xv[e];
     }
-    put8(y + o, r, valid);
+    put8(y + o, r, ncols - col);
   }
 };
 
@@ -164,14 +223,19 @@ struct EpiDcat {
     }
   }
   // attn is a multiple of 8, so a chunk never straddles the O / FC2 border
-  __device__ __forceinline__ void store8(int row, int col, const float (&v)[8], int ncols) const {
+  using Pre = Raw8<T>;
+  __device__ __forceinline__ void pre8(int row, int col, Pre& p, int ncols) const {
+    if (col >= attn) p.load(f + (int64_t)row * ffn + (col - attn), ncols - col);
+  }
+  __device__ __forceinline__ void store8p(int row, int col, const float (&v)[8], const Pre& p,
+                                          int ncols) const {
     const int valid = ncols - col;
     if (col < attn) {
       put8(d_o + (int64_t)row * attn + col, v, valid);
     } else {
       const int c = col - attn;
       float fv[8], r[8];
-      get8(f + (int64_t)row * ffn + c, fv, valid);
+      p.get(f + (int64_t)row * ffn + c, fv, valid);
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = v[e] * gelu_grad_f(fv[e]);
       put8(dz + row * dz_ld + dz_off + c, r, valid);
@@ -527,9 +591,11 @@ __device__ __forceinline__ void wait_barrier() {
 // each wave stages its 32x64 strip in its own LDS area (fp32; block j at
 // word j*kStageBlk + 4j so the row-chunk reads of the two blocks fall on
 // different banks) with a short fully unrolled loop, then re-reads it as
-// 8-column row chunks (8 rows x 64 columns per wave instruction) and runs
-// the epilogue in a rolled loop, so every lane issues 16-byte stores.
-// Contains two workgroup barriers.
+// 8-column row chunks (8 rows x 64 columns per wave instruction, four per
+// lane).  A lane first gathers its four chunks and issues the epilogue's own
+// loads for all of them (pre8), then combines and stores (store8p), so those
+// loads are in flight together instead of one after another.  Every lane
+// issues 16-byte stores.  Contains two workgroup barriers.
 constexpr int kStageRow = 36, kStageBlk = 1216;
 template <class Epi>
 __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* stage, int row0,
@@ -541,15 +607,27 @@ __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* st
     for (int r = 0; r < 16; ++r) blk[mfma32_row(r, lane) * kStageRow + (lane & 31)] = a[j][r];
   }
   __syncthreads();
-#pragma unroll 1
-  for (int c = lane; c < 32 * 8; c += 64) {
+  constexpr int kChunks = 32 * 8 / 64;  // 8-column chunks of the 32x64 strip per lane
+  float v[kChunks][8];
+  typename Epi::Pre pre[kChunks];
+#pragma unroll
+  for (int q = 0; q < kChunks; ++q) {
+    const int c = lane + 64 * q;
     const int rr = c >> 3, jc = c & 7, j = jc >> 2, c8 = (jc & 3) * 8;
     const float* src = stage + j * kStageBlk + j * 4 + rr * kStageRow + c8;
     const float4 lo = *reinterpret_cast<const float4*>(src);
     const float4 hi = *reinterpret_cast<const float4*>(src + 4);
-    const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    v[q][0] = lo.x; v[q][1] = lo.y; v[q][2] = lo.z; v[q][3] = lo.w;
+    v[q][4] = hi.x; v[q][5] = hi.y; v[q][6] = hi.z; v[q][7] = hi.w;
     const int row = row0 + rr, col = col0 + j * 32 + c8;
-    if (row < M && col < N) epi.store8(row, col, v, N);
+    if (row < M && col < N) epi.pre8(row, col, pre[q], N);
+  }
+#pragma unroll
+  for (int q = 0; q < kChunks; ++q) {
+    const int c = lane + 64 * q;
+    const int rr = c >> 3, jc = c & 7, j = jc >> 2, c8 = (jc & 3) * 8;
+    const int row = row0 + rr, col = col0 + j * 32 + c8;
+    if (row < M && col < N) epi.store8p(row, col, v[q], pre[q], N);
   }
   __syncthreads();
 }
