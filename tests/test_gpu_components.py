@@ -118,6 +118,30 @@ def test_gemm_split_schedule(a_layout, b_layout, M, N, K):
         check(f"C(c_f32={c_f32}, split)", _host(outs[0]), ref, "bf16")
 
 
+@pytest.mark.parametrize("a_layout,b_layout", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_gemm_persistent_whole_tiles(a_layout, b_layout):
+    """744 tiles (24 x 31, ragged M, N and K): nearly three whole rounds on
+    256 CUs, so the tiles run persistently, several per workgroup, with no
+    split."""
+    M, N, K = 6096, 7896, 136
+    print(f"gemm persistent layouts={a_layout}{b_layout} M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(11 + a_layout * 2 + b_layout)
+    code, tdt = _dt("bf16")
+    a = _rand(rng, (M, K), "bf16")
+    b = _rand(rng, (N, K), "bf16")
+    ref = a.astype(np.float64) @ b.astype(np.float64).T
+    a_store = a if a_layout == 0 else np.ascontiguousarray(a.T)
+    b_store = b if b_layout == 0 else np.ascontiguousarray(b.T)
+    ad, bd = to_device(a_store, tdt), to_device(b_store, tdt)
+    lda = K if a_layout == 0 else M
+    ldb = K if b_layout == 0 else N
+    ws = torch.empty(B.ptb_gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    c = torch.empty((M, N), dtype=tdt, device="cuda")
+    B.ptb_gemm(code, a_layout, b_layout, M, N, K, ad, lda, bd, ldb, c, N, 0, workspace=ws)
+    torch.cuda.synchronize()
+    check("C(persistent)", _host(c), ref, "bf16")
+
+
 def test_gemm_split_graph_replay():
     """A split-schedule GEMM captured in a graph replays correctly.  The
     launch tag of its split-tile arrival counters is fixed at capture; each

@@ -1023,6 +1023,16 @@ hipError_t run_bf16(const GemmDesc& d, const Epi& epi, hipStream_t s) {
       }
     }
   }
+  // Several rounds of whole tiles: run them persistently (one workgroup per
+  // CU walking its tiles in the same order), which saves a workgroup launch
+  // per tile; the split range is left empty.
+  if (!g.sk && nh == 0 && G >= 8 && tiles > G && tiles % 8 == 0) {
+    g.sk = 1;
+    g.grid = G;
+    g.dp_tiles = tiles;
+    g.sk_base = total;
+    g.sk_iters = 0;
+  }
   if (!g.sk) {
     // Spread the N tiles that run a second K pass evenly over the tile order
     // (heavy tile j at slot floor((2j+1) ntn / 2 nh), light tiles fill the rest).
