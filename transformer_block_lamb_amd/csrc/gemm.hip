@@ -481,7 +481,9 @@ struct Sched {
 // tile to ws and counts itself in the tile's arrival counter; the workgroup
 // that completes the count sums the tile's partials from ws in K order and
 // runs the epilogue, so results do not depend on timing or on which
-// contributor finishes last.
+// contributor finishes last.  With several whole rounds of tiles and no
+// split (dp_tiles = every tile, an empty range), sk == 1 simply walks each
+// CU's tiles in one persistent launch.
 struct GemmArgs {
   const bf16_t* a;
   const bf16_t* b;
