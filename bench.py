@@ -68,6 +68,17 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}))
 
 
+def matrix_params(cfg):
+    """Matrix parameters of the shard: w_in [3A + F, h] plus w_out [A + F, h]."""
+    A, F = cfg.attn_width, cfg.ffn
+    return (3 * A + F) * cfg.hidden + (A + F) * cfg.hidden
+
+
+def model_flops(cfg):
+    """6 * N * T: the model FLOPs of one forward + backward (2N + 4N per token)."""
+    return 6.0 * matrix_params(cfg) * cfg.tokens
+
+
 def stage_flops(cfg):
     """Algorithmic FLOPs of each stage (GEMMs 2*M*N*K; attention over the band)."""
     T, h, A, F = cfg.tokens, cfg.hidden, cfg.attn_width, cfg.ffn
@@ -169,7 +180,7 @@ def time_lamb_shard(params, args, dp=8):
             "hbm_frac": round(nb / (ms * 1e-3) / PEAK_HBM, 4)}
 
 
-def cpu_baseline(cfg, inputs, model_flops):
+def cpu_baseline(cfg, inputs, mflops):
     """The fp64 oracle's forward + backward of one full step of the workload."""
     from oracle import ptb as O
     try:
@@ -184,7 +195,7 @@ def cpu_baseline(cfg, inputs, model_flops):
     O.ptb_backward(d, inputs["x"], inputs["gamma"], inputs["w_in"], inputs["w_out"], saved,
                    inputs["dy"])
     dt = time.perf_counter() - t0
-    return {"value": round(model_flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+    return {"value": round(mflops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"one full forward+backward of the {cfg.name} shard ({cfg.tokens} tokens) "
                       f"in fp64 numpy, model FLOPs 6*N*T over its wall time"}
@@ -309,9 +320,8 @@ def main():
     lamb_shard = None if args.no_lamb_shard else time_lamb_shard(params, args)
 
     flops = stage_flops(cfg)
-    n_mat = (3 * A + F) * cfg.hidden + (A + F) * cfg.hidden
-    model_flops = 6.0 * n_mat * cfg.tokens
-    value = model_flops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+    mflops = model_flops(cfg)
+    value = mflops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
     executed = sum(flops.values()) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
     lb = lamb_bytes(params)
 
@@ -347,11 +357,11 @@ def main():
     if lamb_shard is not None:
         out["lamb_zero2_rank"] = lamb_shard
     if serial is not None:
-        serial["model_tflops"] = round(model_flops / ((serial["fwd_ms"] + serial["bwd_ms"]) * 1e-3)
+        serial["model_tflops"] = round(mflops / ((serial["fwd_ms"] + serial["bwd_ms"]) * 1e-3)
                                        / 1e12, 2)
         out["serial"] = serial
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inputs, model_flops)
+        out["cpu_baseline"] = cpu_baseline(cfg, inputs, mflops)
     line = json.dumps(out)
     print(line, flush=True)
     if args.out:

@@ -24,9 +24,13 @@
  *   - Device pointers must be 16-byte aligned.
  *   - Matrices are row-major.  Activations are token-major [T, width] with
  *     T = batch * seq and the tokens of one sequence contiguous.
- *   - Calls are reentrant.  The only mutable global state is an atomic
+ *   - Calls are reentrant.  The mutable global state is: an atomic
  *     per-process launch counter that tags the split-K arrival counters in
- *     the GEMM workspace (so workspace contents never need initialising).
+ *     the GEMM workspace (so workspace contents never need initialising);
+ *     a per-device cache of the compute-unit count (atomic words, written
+ *     once per device with the same value by any racing caller); and, for
+ *     lamb_step_noalloc only, a per-device static scratch array and the
+ *     cached device address of that array.
  */
 #ifndef PTB_H
 #define PTB_H
@@ -60,8 +64,9 @@ typedef enum { PTB_F32 = 0, PTB_BF16 = 1 } ptb_dtype;
  *                  summed, so their projections fuse into one GEMM)
  *   ln gamma/beta and their gradients are always fp32 [hidden].
  * Constraints: all sizes >= 1; hidden % 8 == 0, ffn % 8 == 0, hidden <= 32768;
- * head_dim in {64, 96, 128}; window >= 1 (window >= seq is plain causal
- * attention); every matrix below 2 GiB.
+ * head_dim in {64, 96, 128}; window >= 1, with no upper bound (any window
+ * >= seq is plain causal attention and gives bit for bit the result of
+ * window = seq); every matrix below 2 GiB.
  * Attention: key j is visible to query i (same sequence) iff 0 <= i-j < window
  * ([MS] SWA row), scores scaled by 1/sqrt(head_dim).  LayerNorm uses the biased
  * variance with ln_eps inside the square root.  GeLU is the exact erf form.
@@ -79,24 +84,32 @@ typedef struct {
   int32_t dtype; /* ptb_dtype */
 } ptb_dims;
 
-/* Bytes of the `saved` buffer that ptb_forward fills and ptb_backward reads
- * (LN output and statistics, Q|K|V, FC1 pre-activation, [O | GeLU(FC1)],
- * attention log-sum-exp; for bf16 also the rounding residuals of the LN
- * output and of q, k, and a 128 MiB + 32 KiB tail that the forward GEMMs
- * use as workspace for split-K partial tiles and their arrival counters).  0 if dims are invalid. */
+/* Bytes of the `saved` buffer that ptb_forward fills and ptb_backward reads:
+ * the activations only (LN output and statistics, Q|K|V, FC1
+ * pre-activation, [O | GeLU(FC1)], attention log-sum-exp; for bf16 also the
+ * rounding residuals of the LN output and of q, k).  175B shard, bf16:
+ * about 189 MB.  0 if dims are invalid. */
 size_t ptb_saved_bytes(const ptb_dims* dims);
 
-/* Bytes of the temporary `scratch` buffer ptb_backward needs (bf16: including
- * 128 MiB + 32 KiB of GEMM split-K workspace).  0 if invalid. */
+/* Bytes of the transient `scratch` buffer (backward temporaries, and for
+ * bf16 128 MiB + 32 KiB of GEMM split-K workspace that the forward uses
+ * too).  One buffer serves ptb_forward and ptb_backward; nothing in it
+ * outlives a call, so calls that share it must be ordered on one stream.
+ * 0 if invalid. */
 size_t ptb_scratch_bytes(const ptb_dims* dims);
 
 /* Forward of one shard ([MS] PTB and SWA rows):
  *   xn = LN(x); [q|k|v|f] = xn w_in^T; O = SWA(q, k, v);
  *   y = [x] + [O | GeLU(f)] w_out.
- * Writes y and `saved` (which must stay untouched until ptb_backward). */
+ * Writes y and `saved` (which must stay untouched until ptb_backward).
+ * scratch: ptb_scratch_bytes(dims) bytes, contents not preserved; or NULL
+ * with scratch_bytes = 0, in which case every GEMM runs whole-tile
+ * schedules (same results up to fp32 summation order, slower at shapes
+ * whose tile count leaves compute units idle). */
 int ptb_forward(const ptb_dims* dims, const void* x, const float* ln_gamma,
                 const float* ln_beta, const void* w_in, const void* w_out, void* y,
-                void* saved, size_t saved_bytes, hipStream_t stream);
+                void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                hipStream_t stream);
 
 /* Backward of one shard: given dy = dL/dy, overwrites dx, d_ln_gamma,
  * d_ln_beta, dw_in, dw_out (same layouts and dtypes as their primal; the LN
@@ -118,15 +131,17 @@ int ptb_backward(const ptb_dims* dims, const void* x, const float* ln_gamma,
  * whole h, so dims->add_residual must be 1 (else PTB_ERR_INVALID_ARG); on a
  * tensor-parallel shard this computes the shard's weights as a whole layer.
  * Buffers and errors as for ptb_forward / ptb_backward; sizes from
- * ptb_serial_saved_bytes / ptb_serial_scratch_bytes (bf16: each includes a
- * 128 MiB + 32 KiB GEMM workspace tail).  Backward overwrites dx, the four LN
- * gradients (fp32), dw_in and dw_out. */
+ * ptb_serial_saved_bytes (activations only) / ptb_serial_scratch_bytes
+ * (bf16: includes the 128 MiB + 32 KiB GEMM workspace; one scratch buffer
+ * serves both calls, and the forward also accepts NULL with 0 bytes).
+ * Backward overwrites dx, the four LN gradients (fp32), dw_in and dw_out. */
 size_t ptb_serial_saved_bytes(const ptb_dims* dims);
 size_t ptb_serial_scratch_bytes(const ptb_dims* dims);
 int ptb_serial_forward(const ptb_dims* dims, const void* x, const float* ln1_gamma,
                        const float* ln1_beta, const float* ln2_gamma, const float* ln2_beta,
                        const void* w_in, const void* w_out, void* y, void* saved,
-                       size_t saved_bytes, hipStream_t stream);
+                       size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                       hipStream_t stream);
 int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_gamma,
                         const float* ln2_gamma, const void* w_in, const void* w_out,
                         const void* saved, size_t saved_bytes, const void* dy, void* dx,
@@ -161,7 +176,9 @@ size_t lamb_scratch_bytes(const lamb_tensor* tensors, int32_t n_tensors);
  *   u = (m / (1-b1^step)) / (sqrt(v / (1-b2^step)) + eps) + weight_decay * w;
  *   r = ||w|| / ||u||  (r = 1 if either norm is 0);  w <- w - lr * r * u.
  * `tensors` is a HOST array of n_tensors descriptors (device pointers inside);
- * step >= 1; 0 <= beta < 1.  ratios_out: optional device float[n_tensors]
+ * step >= 1; 0 <= beta < 1; eps > 0 and finite (with eps = 0 a zero gradient
+ * on zero moments would make u = 0/0, so it is rejected as
+ * PTB_ERR_INVALID_ARG).  ratios_out: optional device float[n_tensors]
  * receiving r.  The norms are exact two-pass reductions: pass A writes m, v
  * and per-workgroup partial sums, a finalize kernel adds them in fp64 in a
  * fixed order (deterministic), pass B recomputes u and applies w. */

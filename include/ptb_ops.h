@@ -44,7 +44,8 @@ enum {
  * stages wrote into `saved` / `scratch`. */
 int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const float* ln_gamma,
                       const float* ln_beta, const void* w_in, const void* w_out, void* y,
-                      void* saved, size_t saved_bytes, hipStream_t stream);
+                      void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                      hipStream_t stream);
 int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const float* ln_gamma,
                        const void* w_in, const void* w_out, const void* saved, size_t saved_bytes,
                        const void* dy, void* dx, float* d_ln_gamma, float* d_ln_beta, void* dw_in,
@@ -58,6 +59,23 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
 int ptb_layernorm_forward(int32_t dtype, int32_t rows, int32_t width, const void* x,
                           const float* gamma, const float* beta, float eps, void* xn,
                           float* mean, float* rstd, hipStream_t stream);
+
+/* Backward of ptb_layernorm_forward for the same x, gamma and the mean, rstd
+ * it wrote: given dxn [rows, width] in `dtype`, writes
+ *   dx = rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)) [+ dy]
+ * with xhat = (x - mean) * rstd and dxhat = dxn * gamma, in `dtype` (dy:
+ * optional residual gradient [rows, width] in `dtype`, NULL = none), and
+ * overwrites dgamma = sum over rows of dxn * xhat and dbeta = sum over rows
+ * of dxn (fp32 [width]); the column sums are added in a fixed order, so the
+ * result is deterministic.  scratch: ptb_layernorm_scratch_bytes(rows,
+ * width) bytes of per-workgroup partial sums, contents not preserved.
+ * width % 8 == 0, width <= 32768. */
+size_t ptb_layernorm_scratch_bytes(int32_t rows, int32_t width);
+int ptb_layernorm_backward(int32_t dtype, int32_t rows, int32_t width, const void* x,
+                           const float* gamma, const float* mean, const float* rstd,
+                           const void* dxn, const void* dy, void* dx, float* dgamma,
+                           float* dbeta, void* scratch, size_t scratch_bytes,
+                           hipStream_t stream);
 
 /* The GEMM engine: C[m, n] = sum_k A(m, k) * B(n, k), for m < M, n < N.
  *   a_layout 0: A(m, k) = a[m*lda + k]      1: A(m, k) = a[k*lda + m]

@@ -43,16 +43,21 @@ def test_workspace_sizes():
     saved = B.ptb_saved_bytes(d)
     assert saved >= 4 * (T * h + T * 3 * A + T * F + T * (A + F)) + 4 * (2 * T + 4 * T)
     assert B.ptb_scratch_bytes(d) > 0
-    # 175B shard, bf16: saved activations about 189 MB (incl. the xn, q, k
-    # residuals) plus the GEMM workspace tail: two fp32 256x256 partial tiles
-    # per persistent workgroup (256) and 4096 8-byte split-tile counters
+    # 175B shard, bf16: `saved` holds the activations only, about 189 MB
+    # (incl. the xn, q, k residuals); the GEMM split-K workspace (two fp32
+    # 256x256 partial tiles per persistent workgroup (256) and 4096 8-byte
+    # split-tile counters) lives in the transient scratch that the forward
+    # and the backward share
     d175 = dims(seq=2048, hidden=12288, n_heads=16, head_dim=96, ffn=6144, window=512, dtype=B.PTB_BF16)
     ws = B.ptb_gemm_workspace_bytes()
     assert ws == 2 * 256 * 256 * 256 * 4 + 4096 * 8
-    assert 185e6 < B.ptb_saved_bytes(d175) - ws < 192e6
+    T, h, A, F = 2048, 12288, 1536, 6144
+    acts = 2 * T * (h + h + 2 * A + 3 * A + F + A + F) + 4 * (2 * T + 16 * T)
+    assert acts <= B.ptb_saved_bytes(d175) < acts + 16 * 256
+    assert 185e6 < B.ptb_saved_bytes(d175) < 192e6
     assert B.ptb_scratch_bytes(d175) > ws
     # fp32 has no split-K workspace
-    assert B.ptb_saved_bytes(d) < ws
+    assert B.ptb_scratch_bytes(d) < ws
 
 
 @pytest.mark.parametrize("bad,status", [
@@ -63,22 +68,41 @@ def test_invalid_dims_rejected_before_launch(bad, status):
     d = dims(**bad)
     assert B.ptb_saved_bytes(d) == 0
     fake = 0x10000
-    r = B.lib().ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    r = B.lib().ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, 1 << 40,
+                            fake, 1 << 40, None)
     assert r == status
+
+
+def test_any_window_is_valid():
+    """window >= seq is plain causal attention, with no upper bound on the
+    window (the library clamps it to the sequence length)."""
+    for w in (128, 129, 4096, 2 ** 31 - 1):
+        assert B.ptb_saved_bytes(dims(window=w)) == B.ptb_saved_bytes(dims())
 
 
 def test_null_unaligned_and_small_workspace_rejected():
     d = dims()
     L = B.lib()
     fake = 0x10000
-    assert L.ptb_forward(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, 1 << 40, None) == -1
-    assert L.ptb_forward(ctypes.byref(d), fake + 2, fake, fake, fake, fake, fake, fake, 1 << 40, None) == -1
+    big = 1 << 40
+    assert L.ptb_forward(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, big, fake, big,
+                         None) == -1
+    assert L.ptb_forward(ctypes.byref(d), fake + 2, fake, fake, fake, fake, fake, fake, big, fake,
+                         big, None) == -1
     need = B.ptb_saved_bytes(d)
-    assert L.ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, need - 1, None) == -3
-    need = B.ptb_scratch_bytes(d)
-    assert L.ptb_backward(ctypes.byref(d), fake, fake, fake, fake, fake, 1 << 40, fake, fake, fake,
-                          fake, fake, fake, fake, need - 1, None) == -3
-    assert L.ptb_forward(None, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None) == -1
+    assert L.ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, need - 1, fake,
+                         big, None) == -3
+    sneed = B.ptb_scratch_bytes(d)
+    # the forward's scratch: the full buffer, or none at all
+    assert L.ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, need, fake,
+                         sneed - 1, None) == -3
+    assert L.ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, need, None,
+                         sneed, None) == -1
+    assert L.ptb_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, need, fake + 4,
+                         sneed, None) == -1
+    assert L.ptb_backward(ctypes.byref(d), fake, fake, fake, fake, fake, big, fake, fake, fake,
+                          fake, fake, fake, fake, sneed - 1, None) == -3
+    assert L.ptb_forward(None, fake, fake, fake, fake, fake, fake, fake, big, fake, big, None) == -1
 
 
 def test_lamb_argument_checks():
@@ -92,6 +116,10 @@ def test_lamb_argument_checks():
     assert L.lamb_step(arr, 2, 1e-3, 0.9, 0.999, 1e-6, 0, None, fake, need, None) == -1   # step 0
     assert L.lamb_step(arr, 2, 1e-3, 1.0, 0.999, 1e-6, 1, None, fake, need, None) == -1   # beta1 1
     assert L.lamb_step(arr, 2, 1e-3, 0.9, 0.999, 1e-6, 1, None, fake, need - 1, None) == -3
+    # eps must be positive and finite (eps = 0 would make u = 0/0 on a zero gradient)
+    for eps in (0.0, -1e-6, float("inf"), float("nan")):
+        assert L.lamb_step(arr, 2, 1e-3, 0.9, 0.999, eps, 1, None, fake, need, None) == -1
+        assert L.lamb_shard_norms(arr, 2, 0.9, 0.999, eps, 1, fake, fake, need, None) == -1
     for bad in (T(100, gdt=5), T(100, w=fake + 4), T(0), T(100, wc=fake + 2)):
         one = (B.LambTensor * 1)(bad)
         assert L.lamb_step(one, 1, 1e-3, 0.9, 0.999, 1e-6, 1, None, fake, need, None) == -1
@@ -136,7 +164,12 @@ def test_serial_block_sizes_and_checks():
     L = B.lib()
     fake = 0x10000
     args = [fake] * 7
-    assert L.ptb_serial_forward(ctypes.byref(d0), *args, fake, fake, 1 << 40, None) == -1
+    big = 1 << 40
+    assert L.ptb_serial_forward(ctypes.byref(d0), *args, fake, fake, big, fake, big, None) == -1
     need = B.ptb_serial_saved_bytes(d)
-    assert L.ptb_serial_forward(ctypes.byref(d), *args, fake, fake, need - 1, None) == -3
-    assert L.ptb_serial_forward(ctypes.byref(d), fake + 4, *args[1:], fake, fake, need, None) == -1
+    sneed = B.ptb_serial_scratch_bytes(d)
+    assert L.ptb_serial_forward(ctypes.byref(d), *args, fake, fake, need - 1, fake, big, None) == -3
+    assert L.ptb_serial_forward(ctypes.byref(d), *args, fake, fake, need, fake, sneed - 1,
+                                None) == -3
+    assert L.ptb_serial_forward(ctypes.byref(d), fake + 4, *args[1:], fake, fake, need, fake, big,
+                                None) == -1

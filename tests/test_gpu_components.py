@@ -50,6 +50,42 @@ def test_layernorm_forward(dtype, rows, width):
     np.testing.assert_allclose(_host(rstd), rrstd, rtol=1e-4)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("residual", [False, True])
+@pytest.mark.parametrize("rows,width", [(1, 8), (37, 264), (130, 4104), (64, 12288), (3, 32768),
+                                        (2500, 264), (1100, 20480), (2048, 12288)])
+def test_layernorm_backward(dtype, residual, rows, width):
+    """ptb_layernorm_backward against the oracle's chain rule, given the
+    oracle's row statistics (so the backward is checked alone); ragged row
+    counts leave the last workgroup's row block partial."""
+    print(f"layernorm backward {dtype} residual={residual} rows={rows} width={width}", flush=True)
+    rng = np.random.default_rng(rows * 11 + width + residual)
+    code, tdt = _dt(dtype)
+    x = _rand(rng, (rows, width), dtype, 2.0)
+    x = bf16_round(x + 0.5) if dtype == "bf16" else x + 0.5
+    g = (1 + 0.1 * rng.standard_normal(width)).astype(np.float32)
+    dxn = _rand(rng, (rows, width), dtype)
+    dy = _rand(rng, (rows, width), dtype) if residual else None
+    _, xhat, mean, rstd = O.layernorm(x, g, np.zeros(width, np.float32), 1e-5)
+    dx_ref, dg_ref, db_ref = O.layernorm_backward(dxn, xhat, rstd, g)
+    if residual:
+        dx_ref = dx_ref + dy
+    xd, gd, dxnd = to_device(x, tdt), to_device(g, torch.float32), to_device(dxn, tdt)
+    dyd = to_device(dy, tdt) if residual else None
+    md = to_device(mean.astype(np.float32), torch.float32)
+    rd = to_device(rstd.astype(np.float32), torch.float32)
+    dx = torch.empty_like(xd)
+    dg = torch.empty(width, dtype=torch.float32, device="cuda")
+    db = torch.empty_like(dg)
+    scratch = torch.empty(B.ptb_layernorm_scratch_bytes(rows, width), dtype=torch.uint8,
+                          device="cuda")
+    B.ptb_layernorm_backward(code, rows, width, xd, gd, md, rd, dxnd, dyd, dx, dg, db, scratch)
+    torch.cuda.synchronize()
+    check("dx", _host(dx), dx_ref, dtype)
+    check("dgamma", _host(dg), dg_ref, dtype)
+    check("dbeta", _host(db), db_ref, dtype)
+
+
 GEMM_SHAPES = [(256, 256, 64), (300, 264, 200), (296, 264, 200), (520, 776, 1032), (40, 24, 8),
                (1, 8, 8), (8, 16, 3), (264, 520, 777)]
 

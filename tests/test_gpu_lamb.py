@@ -148,6 +148,8 @@ def _sharded_vs_full(sizes, n_shards, steps, oracle=False):
     sharded_state = LambState(ts, "bf16", bf16_copy=True)
     sh = ShardedLamb(sharded_state.params, n_shards)
     w0 = [t["w"].astype(np.float64) for t in ts]
+    # largest |w| each element reaches over the steps (the scale of its rounding)
+    wmax = [np.abs(w) for w in w0]
     for s in range(1, steps + 1):
         if s > 1:
             g = lamb_grads(sizes, s)
@@ -155,17 +157,21 @@ def _sharded_vs_full(sizes, n_shards, steps, oracle=False):
             sharded_state.set_grads(g)
         full.step(s, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"])
         sh.step(s, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"])
+        wmax = [np.maximum(m, np.abs(_host(p["w"]))) for m, p in zip(wmax, full.params)]
     torch.cuda.synchronize()
     for i, (pa, pb) in enumerate(zip(full.params, sharded_state.params)):
         # pass A is elementwise: the moments match bit for bit
         assert torch.equal(pa["m"], pb["m"]), i
         assert torch.equal(pa["v"], pb["v"]), i
-        # the norms are added in another order (fp64), which can move the
-        # ratio by an fp32 ulp: w within 3 ulps of the larger of the old and
-        # new magnitudes (w - lr r u can cancel to far below either)
+        # the norms are added in another order (fp64), which can move each
+        # step's fp32 ratio by an ulp, and a step starts from the previous
+        # step's (slightly different) w: w within 3 ulps per step of the
+        # largest magnitude the element reached (w - lr r u can cancel to far
+        # below the magnitudes it was rounded at)
         a, b = _host(pa["w"]), _host(pb["w"])
-        mag = np.maximum(np.abs(a), np.abs(w0[i])).astype(np.float32)
-        assert np.all(np.abs(a - b) <= 3 * np.spacing(mag)), i
+        mag = wmax[i].astype(np.float32)
+        ulps = np.abs(a - b) / np.spacing(mag)
+        assert np.all(ulps <= 3 * steps), (i, float(ulps.max()))
         assert torch.equal(pb["w_bf16"], pb["w"].to(torch.bfloat16)), i
     np.testing.assert_allclose(_host(sh.ratios), _host(full.ratios), rtol=1e-6)
     if oracle:
@@ -181,7 +187,59 @@ def test_lamb_sharded_equals_unsharded(n_shards):
     _sharded_vs_full(SMALL, n_shards, 3)
 
 
-def test_lamb_sharded_175b_dp8():
+
+
+MANY = [1, 3, 4097, 5000, 12, 264, 8192 * 3 + 5, 7, 4096, 100, 2, 999, 16384, 31, 64, 520, 3000,
+        8, 1]
+
+
+def test_lamb_more_tensors_than_one_launch():
+    """19 tensors of mixed sizes: more than one kernel-argument table (16), so
+    the step runs as two batches of launches whose partials, ratios and
+    norms sit at offsets into the scratch and the outputs."""
+    print(f"lamb {len(MANY)} tensors", flush=True)
+    ts = lamb_inputs(MANY)
+    ts[5]["weight_decay"] = 0.0
+    ts[17]["weight_decay"] = 0.1
+    dev = LambState(ts, "bf16")
+    w0 = [t["w"].astype(np.float64) for t in ts]
+    dev.step(1, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"])
+    torch.cuda.synchronize()
+    ref, ratios = _oracle_steps(ts, [[t["g"] for t in ts]], 1)
+    _compare(dev, w0, ref, ratios)
+
+
+@pytest.mark.parametrize("n_shards", [2, 3])
+def test_lamb_sharded_more_tensors_than_one_launch(n_shards):
+    print(f"lamb sharded {len(MANY)} tensors x{n_shards}", flush=True)
+    _sharded_vs_full(MANY, n_shards, 1, oracle=True)
+    _sharded_vs_full(MANY, n_shards, 2)
+
+
+def test_lamb_full_175b_shard_step10():
+    """Step 10 (bias corrections 1 - 0.9^10 and 1 - 0.999^10) on the whole
+    226.5M-parameter shard, from a synthetic mid-training state: moments of
+    the size a few steps of N(0, 1e-3) gradients leave."""
     sizes = [n for _, n in LAMB_175B_TENSORS]
-    print(f"lamb sharded 175B x8 {sum(sizes)} params", flush=True)
-    _sharded_vs_full(sizes, 8, 1)
+    print(f"lamb full 175B shard step 10 {sum(sizes)} params", flush=True)
+    ts = lamb_inputs(sizes)
+    rng = np.random.default_rng(10)
+    for t in ts:
+        n = t["w"].size
+        t["m"] = (3e-4 * rng.standard_normal(n)).astype(np.float32)
+        t["v"] = (1e-6 * rng.standard_normal(n) ** 2 + 1e-8).astype(np.float32)
+    dev = LambState(ts, "bf16")
+    w0 = [t["w"].astype(np.float64) for t in ts]
+    dev.step(10, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"])
+    torch.cuda.synchronize()
+    print("device step done; oracle step", flush=True)
+    ref, ratios = _oracle_steps(ts, [[t["g"] for t in ts]], 10)
+    _compare(dev, w0, ref, ratios)
+
+
+def test_lamb_sharded_175b_dp8_vs_oracle():
+    """ZeRO-2 at DP = 8 over the whole shard, against the oracle (and the
+    unsharded step)."""
+    sizes = [n for _, n in LAMB_175B_TENSORS]
+    print(f"lamb sharded 175B x8 vs oracle {sum(sizes)} params", flush=True)
+    _sharded_vs_full(sizes, 8, 1, oracle=True)

@@ -31,11 +31,11 @@ RAGGED = [
 ]
 
 
-def run_case(cfg, ln_affine="random"):
-    print(f"ptb case {cfg}", flush=True)
+def run_case(cfg, ln_affine="random", use_scratch=True):
+    print(f"ptb case {cfg} scratch={use_scratch}", flush=True)
     inp = ptb_inputs(cfg, ln_affine=ln_affine)
     shard = PtbShard(cfg, inp)
-    shard.forward()
+    shard.forward(use_scratch=use_scratch)
     shard.backward()
     torch.cuda.synchronize()
     got = shard.outputs()
@@ -80,4 +80,68 @@ def test_deterministic_bitwise():
 
 @pytest.mark.parametrize("name", ["175b_w512", "175b_w2048", "small", "530b_w512"])
 def test_full_size(name):
-    run_case(CONFIGS[name], ln_affine="unit")
+    run_case(CONFIGS[name], ln_affine="random")
+
+
+def test_forward_without_scratch():
+    """ptb_forward with no scratch runs every GEMM on whole-tile schedules;
+    the shape is one whose input projection otherwise splits."""
+    run_case(RAGGED[6], use_scratch=False)
+
+
+@pytest.mark.parametrize("cfg", [RAGGED[0], RAGGED[5]], ids=lambda c: c.name)
+def test_window_beyond_seq_is_causal_bitwise(cfg):
+    """Any window >= seq is plain causal attention: window = 2^31 - 1 gives
+    bit for bit the outputs of window = seq (bf16 and fp32)."""
+    print(f"window beyond seq {cfg.name}", flush=True)
+    inp = ptb_inputs(cfg, ln_affine="random")
+    outs = []
+    for w in (cfg.seq, 2 ** 31 - 1):
+        shard = PtbShard(cfg.replace(window=w), inp)
+        shard.forward()
+        shard.backward()
+        torch.cuda.synchronize()
+        outs.append({k: getattr(shard, k).clone() for k in ("y", "dx", "dgamma", "dbeta", "dw_in",
+                                                            "dw_out")})
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), k
+
+
+def test_tensor_parallel_shards_sum_to_full_layer():
+    """A full layer of 16 heads x 64 and FFN 1088 split into 8 tensor-parallel
+    shards (row blocks of w_in and w_out), each run through ptb_forward /
+    ptb_backward with the residual on shard 0 only: the shards' y, dx,
+    dgamma, dbeta summed on the device match the oracle's unsharded layer,
+    and each shard's weight gradients match the rows of the full ones."""
+    n, Hf, d, Ff = 8, 16, 64, 1088
+    full = PtbConfig("tp_full", 2, 200, 264, Hf, d, Ff, 50, "bf16", 1)
+    print(f"tp shards {full}", flush=True)
+    inp = ptb_inputs(full, ln_affine="random")
+    A, Hs, Fs = Hf * d, Hf // n, Ff // n
+    As = Hs * d
+    dm = O.dims_of(full)
+    y, saved = O.ptb_forward(dm, inp["x"], inp["gamma"], inp["beta"], inp["w_in"], inp["w_out"])
+    g = O.ptb_backward(dm, inp["x"], inp["gamma"], inp["w_in"], inp["w_out"], saved, inp["dy"])
+    sums = {k: None for k in ("y", "dx", "dgamma", "dbeta")}
+    allow = 0.0  # each shard's y is rounded to bf16 before the sum
+    for r in range(n):
+        blk = lambda base: np.arange(base + r * As, base + (r + 1) * As)
+        rows = np.concatenate([blk(0), blk(A), blk(2 * A), 3 * A + np.arange(r * Fs, (r + 1) * Fs)])
+        out_rows = np.concatenate([blk(0), A + np.arange(r * Fs, (r + 1) * Fs)])
+        cfg = full.replace(name=f"tp{r}", n_heads=Hs, ffn=Fs, add_residual=int(r == 0))
+        shard = PtbShard(cfg, dict(inp, w_in=inp["w_in"][rows], w_out=inp["w_out"][out_rows]))
+        shard.forward()
+        shard.backward()
+        for k in sums:
+            t = getattr(shard, k).float()
+            sums[k] = t if sums[k] is None else sums[k] + t
+        torch.cuda.synchronize()
+        got = shard.outputs()
+        allow = allow + half_ulp(got["y"], "bf16")
+        check(f"dw_in[{r}]", got["dw_in"], g["dw_in"][rows], "bf16")
+        check(f"dw_out[{r}]", got["dw_out"], g["dw_out"][out_rows], "bf16")
+    host = {k: v.cpu().numpy().astype(np.float64) for k, v in sums.items()}
+    check("sum y", host["y"], y, "bf16")
+    check("sum y - x", host["y"] - inp["x"], y - inp["x"], "bf16", allow)
+    for k in ("dx", "dgamma", "dbeta"):
+        check(f"sum {k}", host[k], g[k], "bf16")

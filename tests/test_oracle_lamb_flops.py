@@ -102,7 +102,98 @@ def test_band_pairs_brute_force(s, w):
     assert flops.band_pairs(s, s) == s * (s + 1) // 2
 
 
-def test_attention_flops_175b():
-    # 16 heads of 96 at s = 2048: 917,760 band pairs per head at w = 512
-    assert flops.band_pairs(2048, 512) == 917_760
-    assert flops.attention_flops_fwd(1, 2048, 16, 96, 512) == pytest.approx(4 * 96 * 917_760 * 16)
+def _loop_attention(q, k, v, d_o, window):
+    """Banded attention of one head, forward and backward, as explicit loops
+    over the visible (query, key) pairs only.  Returns (O, dQ, dK, dV) and
+    the multiply-adds of the d-long products: forward Q K^T and P V, backward
+    dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q.  (Row softmax
+    statistics and D_i = sum_j P_ij dP_ij are O(pairs), not O(pairs * d), and
+    are not part of the band FLOPs.)"""
+    s, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    fwd = bwd = 0
+    vis = [[j for j in range(s) if 0 <= i - j < window] for i in range(s)]
+    P, O = {}, np.zeros((s, d))
+    for i in range(s):
+        sc = {}
+        for j in vis[i]:
+            acc = 0.0
+            for c in range(d):
+                acc += q[i, c] * k[j, c]
+                fwd += 1
+            sc[j] = acc * scale
+        mx = max(sc.values())
+        z = sum(math.exp(x - mx) for x in sc.values())
+        for j in vis[i]:
+            P[i, j] = math.exp(sc[j] - mx) / z
+            for c in range(d):
+                O[i, c] += P[i, j] * v[j, c]
+                fwd += 1
+    dQ, dK, dV = np.zeros((s, d)), np.zeros((s, d)), np.zeros((s, d))
+    for i in range(s):
+        dP = {}
+        for j in vis[i]:
+            acc = 0.0
+            for c in range(d):
+                acc += d_o[i, c] * v[j, c]
+                bwd += 1
+            dP[j] = acc
+            for c in range(d):
+                dV[j, c] += P[i, j] * d_o[i, c]
+                bwd += 1
+        D = sum(P[i, j] * dP[j] for j in vis[i])
+        for j in vis[i]:
+            ds = P[i, j] * (dP[j] - D) * scale
+            for c in range(d):
+                dQ[i, c] += ds * k[j, c]
+                dK[j, c] += ds * q[i, c]
+                bwd += 2
+    return O, dQ, dK, dV, fwd, bwd
+
+
+@pytest.mark.parametrize("b,s,H,d,w", [(1, 9, 1, 3, 4), (2, 7, 2, 2, 1), (1, 6, 3, 4, 6),
+                                         (1, 5, 1, 2, 40)])
+def test_attention_flops_count_the_band_products(b, s, H, d, w):
+    """attention_flops_fwd / _bwd equal twice the multiply-adds that a loop
+    implementation performs over the visible pairs, and that loop
+    implementation computes the oracle's attention and gradients."""
+    rng = np.random.default_rng(s * 31 + w)
+    fwd = bwd = 0
+    for _ in range(b * H):
+        q, k, v, d_o = (rng.standard_normal((s, d)) for _ in range(4))
+        O, dQ, dK, dV, f, g = _loop_attention(q, k, v, d_o, w)
+        o_ref, p_ref, _ = ptb.swa_head(q, k, v, w)
+        np.testing.assert_allclose(O, o_ref, rtol=1e-12, atol=1e-14)
+        dq_ref, dk_ref, dv_ref = ptb.swa_head_backward(q, k, v, p_ref, d_o)
+        for got, ref in ((dQ, dq_ref), (dK, dk_ref), (dV, dv_ref)):
+            np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+        fwd += f
+        bwd += g
+    assert flops.attention_flops_fwd(b, s, H, d, w) == 2 * fwd
+    assert flops.attention_flops_bwd(b, s, H, d, w) == 2 * bwd
+
+
+def test_band_pairs_175b():
+    """16 heads of 96 at s = 2048: 917,760 band pairs per head at w = 512 and
+    2,098,176 (plain causal) at w = 2048, counted from the visibility mask."""
+    assert flops.band_pairs(2048, 512) == int(ptb.swa_visible(2048, 512).sum()) == 917_760
+    assert flops.band_pairs(2048, 2048) == int(ptb.swa_visible(2048, 2048).sum()) == 2_098_176
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "175b_w512", "175b_w2048", "530b_w512"])
+def test_bench_flop_arithmetic_matches_oracle(name):
+    """The FLOP figures bench.py reports come from its own arithmetic (the
+    product path may not import the oracle); they must equal oracle.flops."""
+    import bench
+    from transformer_block_lamb_amd.synth import CONFIGS
+    cfg = CONFIGS[name]
+    n_mat = flops.shard_matrix_params(cfg.hidden, cfg.attn_width, cfg.ffn)
+    assert bench.matrix_params(cfg) == n_mat
+    assert bench.model_flops(cfg) == flops.model_flops(n_mat, cfg.tokens)
+    st = bench.stage_flops(cfg)
+    gemms = sum(v for k, v in st.items() if "gemm" in k)
+    assert gemms == pytest.approx(flops.model_flops(n_mat, cfg.tokens), rel=1e-15)
+    args = (cfg.batch, cfg.seq, cfg.n_heads, cfg.head_dim, cfg.window)
+    assert st["fwd.attention"] == flops.attention_flops_fwd(*args)
+    assert st["bwd.attention"] == flops.attention_flops_bwd(*args)
+    assert st["fwd.layernorm"] == st["bwd.layernorm"] == 0.0

@@ -23,7 +23,8 @@ EXPORTED = ("ptb_saved_bytes", "ptb_scratch_bytes", "ptb_forward", "ptb_backward
             "ptb_forward_stage", "ptb_backward_stage",
             "ptb_layernorm_forward", "ptb_gemm_workspace_bytes", "ptb_gemm", "ptb_swa_forward",
             "ptb_swa_backward", "ptb_serial_saved_bytes", "ptb_serial_scratch_bytes",
-            "ptb_serial_forward", "ptb_serial_backward", "lamb_shard_norms", "lamb_shard_apply")
+            "ptb_serial_forward", "ptb_serial_backward", "lamb_shard_norms", "lamb_shard_apply",
+            "ptb_layernorm_scratch_bytes", "ptb_layernorm_backward")
 FWD_STAGES = ("layernorm", "gemm_in", "attention", "gemm_out")
 BWD_STAGES = ("gemm_dcat", "gemm_dw_out", "attention", "gemm_dw_in", "gemm_dxn", "layernorm")
 
@@ -65,10 +66,11 @@ def lib():
         sig = {
             "ptb_saved_bytes": (sz, [pd]),
             "ptb_scratch_bytes": (sz, [pd]),
-            "ptb_forward": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ptb_forward": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]),
             "ptb_backward": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
                                             vp, sz, vp]),
-            "ptb_forward_stage": (ctypes.c_int, [pd, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ptb_forward_stage": (ctypes.c_int, [pd, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz,
+                                                 vp]),
             "ptb_backward_stage": (ctypes.c_int, [pd, i32, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp,
                                                   vp, vp, vp, sz, vp]),
             "lamb_scratch_bytes": (sz, [pl, i32]),
@@ -79,6 +81,9 @@ def lib():
             "ptb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "ptb_layernorm_forward": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp,
                                                      vp]),
+            "ptb_layernorm_scratch_bytes": (sz, [i32, i32]),
+            "ptb_layernorm_backward": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                      vp, vp, vp, sz, vp]),
             "ptb_gemm_workspace_bytes": (ctypes.c_size_t, []),
             "ptb_gemm": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64,
                                         i32, vp, ctypes.c_size_t, vp]),
@@ -86,7 +91,8 @@ def lib():
             "ptb_swa_backward": (ctypes.c_int, [pd, vp, vp, i64, vp, vp, vp, vp, vp]),
             "ptb_serial_saved_bytes": (sz, [pd]),
             "ptb_serial_scratch_bytes": (sz, [pd]),
-            "ptb_serial_forward": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ptb_serial_forward": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                  sz, vp]),
             "ptb_serial_backward": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp,
                                                    vp, vp, vp, vp, vp, sz, vp]),
         }
@@ -144,10 +150,16 @@ def ptb_scratch_bytes(dims: PtbDims) -> int:
     return lib().ptb_scratch_bytes(ctypes.byref(dims))
 
 
-def ptb_forward(dims, x, ln_gamma, ln_beta, w_in, w_out, y, saved, stream=None):
+def _opt_nbytes(t):
+    return 0 if t is None else _nbytes(t)
+
+
+def ptb_forward(dims, x, ln_gamma, ln_beta, w_in, w_out, y, saved, scratch, stream=None):
+    """scratch: the ptb_scratch_bytes buffer (also used by ptb_backward), or
+    None for whole-tile GEMM schedules."""
     _check(lib().ptb_forward(ctypes.byref(dims), _ptr(x), _ptr(ln_gamma), _ptr(ln_beta),
-                             _ptr(w_in), _ptr(w_out), _ptr(y), _ptr(saved),
-                             saved.numel() * saved.element_size(), _stream(stream)),
+                             _ptr(w_in), _ptr(w_out), _ptr(y), _ptr(saved), _nbytes(saved),
+                             _ptr(scratch), _opt_nbytes(scratch), _stream(stream)),
            "ptb_forward")
 
 
@@ -161,10 +173,12 @@ def ptb_backward(dims, x, ln_gamma, w_in, w_out, saved, dy, dx, d_ln_gamma, d_ln
            "ptb_backward")
 
 
-def ptb_forward_stage(dims, stage, x, ln_gamma, ln_beta, w_in, w_out, y, saved, stream=None):
+def ptb_forward_stage(dims, stage, x, ln_gamma, ln_beta, w_in, w_out, y, saved, scratch,
+                      stream=None):
     _check(lib().ptb_forward_stage(ctypes.byref(dims), stage, _ptr(x), _ptr(ln_gamma),
                                    _ptr(ln_beta), _ptr(w_in), _ptr(w_out), _ptr(y), _ptr(saved),
-                                   saved.numel() * saved.element_size(), _stream(stream)),
+                                   _nbytes(saved), _ptr(scratch), _opt_nbytes(scratch),
+                                   _stream(stream)),
            f"ptb_forward_stage({stage})")
 
 
@@ -232,6 +246,19 @@ def ptb_layernorm_forward(dtype, rows, width, x, gamma, beta, eps, xn, mean, rst
            "ptb_layernorm_forward")
 
 
+def ptb_layernorm_scratch_bytes(rows, width) -> int:
+    return int(lib().ptb_layernorm_scratch_bytes(rows, width))
+
+
+def ptb_layernorm_backward(dtype, rows, width, x, gamma, mean, rstd, dxn, dy, dx, dgamma, dbeta,
+                           scratch, stream=None):
+    _check(lib().ptb_layernorm_backward(dtype, rows, width, _ptr(x), _ptr(gamma), _ptr(mean),
+                                        _ptr(rstd), _ptr(dxn), _ptr(dy), _ptr(dx), _ptr(dgamma),
+                                        _ptr(dbeta), _ptr(scratch), _nbytes(scratch),
+                                        _stream(stream)),
+           "ptb_layernorm_backward")
+
+
 def ptb_gemm_workspace_bytes():
     return int(lib().ptb_gemm_workspace_bytes())
 
@@ -264,10 +291,11 @@ def ptb_serial_scratch_bytes(dims: PtbDims) -> int:
 
 
 def ptb_serial_forward(dims, x, ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, w_in, w_out, y, saved,
-                       stream=None):
+                       scratch, stream=None):
     _check(lib().ptb_serial_forward(ctypes.byref(dims), _ptr(x), _ptr(ln1_gamma), _ptr(ln1_beta),
                                     _ptr(ln2_gamma), _ptr(ln2_beta), _ptr(w_in), _ptr(w_out),
-                                    _ptr(y), _ptr(saved), _nbytes(saved), _stream(stream)),
+                                    _ptr(y), _ptr(saved), _nbytes(saved), _ptr(scratch),
+                                    _opt_nbytes(scratch), _stream(stream)),
            "ptb_serial_forward")
 
 

@@ -58,7 +58,7 @@ struct Dims {
 // the attention scores are formed at fp32-level accuracy (see the input
 // GEMM and the attention kernels).
 struct SavedLayout {
-  size_t xn, xn_lo, qk_lo, qkv, f, cat, mean, rstd, lse, gemm_ws, total;
+  size_t xn, xn_lo, qk_lo, qkv, f, cat, mean, rstd, lse, total;
   explicit SavedLayout(const Dims& d) {
     const bool split = d.e == 2;
     size_t o = 0;
@@ -71,12 +71,13 @@ struct SavedLayout {
     mean = o; o += up(d.T * 4);
     rstd = o; o += up(d.T * 4);
     lse = o;  o += up(d.B * d.H * d.S * 4);
-    gemm_ws = o; o += split ? kGemmWsBytes : 0;  // transient, forward GEMMs only
     total = o;
   }
 };
 
-// Backward temporaries.
+// Temporaries of one call: the backward's intermediate gradients, and the
+// split-K workspace of the GEMMs, which the forward uses too.  Nothing in it
+// outlives a call.
 struct ScratchLayout {
   size_t d_o, dz, dxn, dvec, gpart, bpart, gemm_ws, total;
   explicit ScratchLayout(const Dims& d) {
@@ -92,6 +93,23 @@ struct ScratchLayout {
     total = o;
   }
 };
+
+// The attention descriptor of a call.  A window of at least the sequence
+// length is plain causal attention, so it is clamped to the sequence length
+// here once: the kernels' band arithmetic (query index + window - 1) then
+// stays far from the int32 range whatever window the caller passes.
+SwaDesc swa_desc(const ptb_dims* dims, const void* qkv, int64_t ld_qkv, const void* qk_lo) {
+  const int w = dims->window < dims->seq ? dims->window : dims->seq;
+  return SwaDesc{dims->batch, dims->seq, dims->n_heads, dims->head_dim, w, qkv, ld_qkv, qk_lo};
+}
+
+// The forward's scratch is optional: null with 0 bytes runs every GEMM on
+// whole-tile schedules; otherwise it must be the full, aligned buffer.
+int check_fwd_scratch(const void* scratch, size_t bytes, size_t need) {
+  if (scratch == nullptr) return bytes == 0 ? PTB_OK : PTB_ERR_INVALID_ARG;
+  if (!aligned16(scratch)) return PTB_ERR_INVALID_ARG;
+  return bytes >= need ? PTB_OK : PTB_ERR_WORKSPACE;
+}
 
 template <typename T>
 T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
@@ -135,14 +153,18 @@ size_t ptb_scratch_bytes(const ptb_dims* d) {
 
 int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const float* ln_gamma,
                       const float* ln_beta, const void* w_in, const void* w_out, void* y,
-                      void* saved, size_t saved_bytes, hipStream_t stream) {
+                      void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                      hipStream_t stream) {
   int st = check_dims(dims);
   if (st != PTB_OK) return st;
   if (stage < -1 || stage >= PTB_FWD_STAGES) return PTB_ERR_INVALID_ARG;
   if (!all_aligned({x, ln_gamma, ln_beta, w_in, w_out, y, saved})) return PTB_ERR_INVALID_ARG;
   const Dims d(dims);
   const SavedLayout L(d);
+  const ScratchLayout R(d);
   if (saved_bytes < L.total) return PTB_ERR_WORKSPACE;
+  st = check_fwd_scratch(scratch, scratch_bytes, R.total);
+  if (st != PTB_OK) return st;
   const int dt = dims->dtype;
   void* xn = at<char>(saved, L.xn);
   void* xn_lo = dt == PTB_BF16 ? at<char>(saved, L.xn_lo) : nullptr;
@@ -153,10 +175,9 @@ int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const 
   float* mean = at<float>(saved, L.mean);
   float* rstd = at<float>(saved, L.rstd);
   float* lse = at<float>(saved, L.lse);
-  void* ws = dt == PTB_BF16 ? at<char>(saved, L.gemm_ws) : nullptr;
-  const size_t ws_bytes = dt == PTB_BF16 ? kGemmWsBytes : 0;
-  const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
-                   3 * d.A, qk_lo};
+  void* ws = dt == PTB_BF16 && scratch != nullptr ? at<char>(scratch, R.gemm_ws) : nullptr;
+  const size_t ws_bytes = ws != nullptr ? kGemmWsBytes : 0;
+  const SwaDesc sw = swa_desc(dims, qkv, 3 * d.A, qk_lo);
   for (int s = (stage < 0 ? 0 : stage); s < (stage < 0 ? PTB_FWD_STAGES : stage + 1); ++s) {
     hipError_t e = hipSuccess;
     switch (s) {
@@ -193,9 +214,9 @@ int ptb_forward_stage(const ptb_dims* dims, int32_t stage, const void* x, const 
 
 int ptb_forward(const ptb_dims* dims, const void* x, const float* ln_gamma, const float* ln_beta,
                 const void* w_in, const void* w_out, void* y, void* saved, size_t saved_bytes,
-                hipStream_t stream) {
+                void* scratch, size_t scratch_bytes, hipStream_t stream) {
   return ptb_forward_stage(dims, -1, x, ln_gamma, ln_beta, w_in, w_out, y, saved, saved_bytes,
-                           stream);
+                           scratch, scratch_bytes, stream);
 }
 
 int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const float* ln_gamma,
@@ -229,8 +250,7 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
   float* bpart = at<float>(scratch, R.bpart);
   void* ws = dt == PTB_BF16 ? at<char>(scratch, R.gemm_ws) : nullptr;
   const size_t ws_bytes = dt == PTB_BF16 ? kGemmWsBytes : 0;
-  const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
-                   3 * d.A, qk_lo};
+  const SwaDesc sw = swa_desc(dims, qkv, 3 * d.A, qk_lo);
   for (int s = (stage < 0 ? 0 : stage); s < (stage < 0 ? PTB_BWD_STAGES : stage + 1); ++s) {
     hipError_t e = hipSuccess;
     switch (s) {
@@ -294,8 +314,7 @@ int ptb_backward(const ptb_dims* dims, const void* x, const float* ln_gamma, con
 namespace {
 
 struct SerialSavedLayout {
-  size_t xn1, xn1_lo, qk_lo, qkv, cat, hid, xn2, f, mean1, rstd1, mean2, rstd2, lse, gemm_ws,
-      total;
+  size_t xn1, xn1_lo, qk_lo, qkv, cat, hid, xn2, f, mean1, rstd1, mean2, rstd2, lse, total;
   explicit SerialSavedLayout(const Dims& d) {
     const bool split = d.e == 2;
     size_t o = 0;
@@ -312,7 +331,6 @@ struct SerialSavedLayout {
     mean2 = o;  o += up(d.T * 4);
     rstd2 = o;  o += up(d.T * 4);
     lse = o;    o += up(d.B * d.H * d.S * 4);
-    gemm_ws = o; o += split ? kGemmWsBytes : 0;
     total = o;
   }
 };
@@ -360,14 +378,18 @@ size_t ptb_serial_scratch_bytes(const ptb_dims* d) {
 int ptb_serial_forward(const ptb_dims* dims, const void* x, const float* ln1_gamma,
                        const float* ln1_beta, const float* ln2_gamma, const float* ln2_beta,
                        const void* w_in, const void* w_out, void* y, void* saved,
-                       size_t saved_bytes, hipStream_t stream) {
+                       size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                       hipStream_t stream) {
   int st = check_serial_dims(dims);
   if (st != PTB_OK) return st;
   if (!all_aligned({x, ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, w_in, w_out, y, saved}))
     return PTB_ERR_INVALID_ARG;
   const Dims d(dims);
   const SerialSavedLayout L(d);
+  const SerialScratchLayout R(d);
   if (saved_bytes < L.total) return PTB_ERR_WORKSPACE;
+  st = check_fwd_scratch(scratch, scratch_bytes, R.total);
+  if (st != PTB_OK) return st;
   const int dt = dims->dtype;
   const bool bf = dt == PTB_BF16;
   void* xn1 = at<char>(saved, L.xn1);
@@ -378,10 +400,9 @@ int ptb_serial_forward(const ptb_dims* dims, const void* x, const float* ln1_gam
   void* hid = at<char>(saved, L.hid);
   void* xn2 = at<char>(saved, L.xn2);
   void* f = at<char>(saved, L.f);
-  void* ws = bf ? at<char>(saved, L.gemm_ws) : nullptr;
-  const size_t wsb = bf ? kGemmWsBytes : 0;
-  const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
-                   3 * d.A, qk_lo};
+  void* ws = bf && scratch != nullptr ? at<char>(scratch, R.gemm_ws) : nullptr;
+  const size_t wsb = ws != nullptr ? kGemmWsBytes : 0;
+  const SwaDesc sw = swa_desc(dims, qkv, 3 * d.A, qk_lo);
   hipError_t e = launch_ln_fwd(dt, x, ln1_gamma, ln1_beta, dims->ln_eps, (int)d.T, (int)d.h, xn1,
                                xn1_lo, at<float>(saved, L.mean1), at<float>(saved, L.rstd1),
                                stream);
@@ -453,8 +474,7 @@ int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_ga
   void* ws = bf ? at<char>(scratch, R.gemm_ws) : nullptr;
   const size_t wsb = bf ? kGemmWsBytes : 0;
   const int nblk = (int)((d.T + ln_bwd_rows_per_block() - 1) / ln_bwd_rows_per_block());
-  const SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv,
-                   3 * d.A, qk_lo};
+  const SwaDesc sw = swa_desc(dims, qkv, 3 * d.A, qk_lo);
   auto gemm = [&](int M, int N, int K, int al, int bl, const void* a, int64_t lda, const void* b,
                   int64_t ldb) {
     GemmDesc g{M, N, K, al, bl, a, lda, b, ldb};
@@ -533,8 +553,9 @@ int lamb_check(const lamb_tensor* t, int32_t n, float lr, float beta1, float bet
                int64_t step, void* scratch, size_t scratch_bytes, bool need_grad, LambHyper& hp,
                int64_t& total_blocks) {
   if (t == nullptr || n < 1 || step < 1) return PTB_ERR_INVALID_ARG;
-  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f &&
-        isfinite(lr)))
+  // eps > 0: with eps = 0 a zero gradient on fresh moments makes u = 0 / 0
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps > 0.f &&
+        isfinite(eps) && isfinite(lr)))
     return PTB_ERR_INVALID_ARG;
   if (scratch == nullptr || !aligned16(scratch)) return PTB_ERR_INVALID_ARG;
   total_blocks = 0;
@@ -647,6 +668,34 @@ int ptb_layernorm_forward(int32_t dtype, int32_t rows, int32_t width, const void
       launch_ln_fwd(dtype, x, gamma, beta, eps, rows, width, xn, nullptr, mean, rstd, stream));
 }
 
+size_t ptb_layernorm_scratch_bytes(int32_t rows, int32_t width) {
+  if (rows < 1 || width < 8 || width % 8 != 0 || width > 32768) return 0;
+  const int64_t nblk = ((int64_t)rows + ln_bwd_rows_per_block() - 1) / ln_bwd_rows_per_block();
+  return 2 * up((size_t)nblk * width * 4);
+}
+
+int ptb_layernorm_backward(int32_t dtype, int32_t rows, int32_t width, const void* x,
+                           const float* gamma, const float* mean, const float* rstd,
+                           const void* dxn, const void* dy, void* dx, float* dgamma,
+                           float* dbeta, void* scratch, size_t scratch_bytes,
+                           hipStream_t stream) {
+  if (dtype != PTB_F32 && dtype != PTB_BF16) return PTB_ERR_INVALID_ARG;
+  const size_t need = ptb_layernorm_scratch_bytes(rows, width);
+  if (need == 0) return PTB_ERR_INVALID_ARG;
+  if ((int64_t)rows * width * 4 >= kMaxMatrixBytes) return PTB_ERR_UNSUPPORTED;
+  if (!all_aligned({x, gamma, mean, rstd, dxn, dx, dgamma, dbeta, scratch}))
+    return PTB_ERR_INVALID_ARG;
+  if (dy != nullptr && !aligned16(dy)) return PTB_ERR_INVALID_ARG;
+  if (scratch_bytes < need) return PTB_ERR_WORKSPACE;
+  const int nblk = (rows + ln_bwd_rows_per_block() - 1) / ln_bwd_rows_per_block();
+  float* gpart = static_cast<float*>(scratch);
+  float* bpart = at<float>(scratch, need / 2);
+  hipError_t e = launch_ln_bwd(dtype, x, gamma, mean, rstd, dxn, dy, dx, gpart, bpart, rows,
+                               width, stream);
+  if (e == hipSuccess) e = launch_ln_bwd_reduce(gpart, bpart, nblk, width, dgamma, dbeta, stream);
+  return hip_status(e);
+}
+
 size_t ptb_gemm_workspace_bytes(void) { return kGemmWsBytes; }
 
 int ptb_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t M, int32_t N, int32_t K,
@@ -685,7 +734,7 @@ int ptb_swa_forward(const ptb_dims* dims, const void* qkv, void* o, int64_t ldo,
   if (!all_aligned({qkv, o, lse})) return PTB_ERR_INVALID_ARG;
   const Dims d(dims);
   if (ldo < d.A || ldo % 8) return PTB_ERR_INVALID_ARG;
-  SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv, 3 * d.A};
+  const SwaDesc sw = swa_desc(dims, qkv, 3 * d.A, nullptr);
   return hip_status(launch_swa_fwd(dims->dtype, sw, o, ldo, lse, stream));
 }
 
@@ -697,7 +746,7 @@ int ptb_swa_backward(const ptb_dims* dims, const void* qkv, const void* o, int64
   if (!all_aligned({qkv, o, d_o, lse, dqkv, dvec})) return PTB_ERR_INVALID_ARG;
   const Dims d(dims);
   if (ldo < d.A || ldo % 8) return PTB_ERR_INVALID_ARG;
-  SwaDesc sw{dims->batch, dims->seq, dims->n_heads, dims->head_dim, dims->window, qkv, 3 * d.A};
+  const SwaDesc sw = swa_desc(dims, qkv, 3 * d.A, nullptr);
   return hip_status(
       launch_swa_bwd(dims->dtype, sw, o, ldo, d_o, d.A, lse, dvec, dqkv, 3 * d.A, stream));
 }

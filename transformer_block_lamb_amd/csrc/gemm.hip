@@ -928,18 +928,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 g, Epi epi) {
 // --------------------------------------------------------------- dispatch
 // Workgroups of a persistent launch: the CU count of the current device,
 // rounded down to a multiple of the 8 XCDs, at most kSkMaxGrid (0 if unknown).
+// The per-device cache is atomic: racing first calls store the same value.
 int persistent_grid() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
+  int c = cached[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     cus = (cus < kSkMaxGrid ? cus : kSkMaxGrid) & ~7;
-    cached[dev] = cus > 0 ? cus : -1;
+    c = cus > 0 ? cus : -1;
+    cached[dev].store(c, std::memory_order_relaxed);
   }
-  return cached[dev] > 0 ? cached[dev] : 0;
+  return c > 0 ? c : 0;
 }
 
 // A 48-bit tag per split launch, so arrival counters left by earlier

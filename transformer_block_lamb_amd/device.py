@@ -40,9 +40,9 @@ class PtbShard:
         self.saved = torch.empty(B.ptb_saved_bytes(self.dims), dtype=torch.uint8, device=device)
         self.scratch = torch.empty(B.ptb_scratch_bytes(self.dims), dtype=torch.uint8, device=device)
 
-    def forward(self, stream=None):
+    def forward(self, stream=None, use_scratch=True):
         B.ptb_forward(self.dims, self.x, self.gamma, self.beta, self.w_in, self.w_out, self.y,
-                      self.saved, stream)
+                      self.saved, self.scratch if use_scratch else None, stream)
 
     def backward(self, stream=None):
         B.ptb_backward(self.dims, self.x, self.gamma, self.w_in, self.w_out, self.saved, self.dy,
@@ -51,7 +51,7 @@ class PtbShard:
 
     def forward_stage(self, stage, stream=None):
         B.ptb_forward_stage(self.dims, stage, self.x, self.gamma, self.beta, self.w_in,
-                            self.w_out, self.y, self.saved, stream)
+                            self.w_out, self.y, self.saved, self.scratch, stream)
 
     def backward_stage(self, stage, stream=None):
         B.ptb_backward_stage(self.dims, stage, self.x, self.gamma, self.w_in, self.w_out,
@@ -80,9 +80,10 @@ class SerialShard(PtbShard):
         self.scratch = torch.empty(B.ptb_serial_scratch_bytes(self.dims), dtype=torch.uint8,
                                    device=device)
 
-    def forward(self, stream=None):
+    def forward(self, stream=None, use_scratch=True):
         B.ptb_serial_forward(self.dims, self.x, self.gamma, self.beta, self.gamma2, self.beta2,
-                             self.w_in, self.w_out, self.y, self.saved, stream)
+                             self.w_in, self.w_out, self.y, self.saved,
+                             self.scratch if use_scratch else None, stream)
 
     def backward(self, stream=None):
         B.ptb_serial_backward(self.dims, self.x, self.gamma, self.gamma2, self.w_in, self.w_out,
