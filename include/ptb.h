@@ -214,6 +214,24 @@ int lamb_shard_apply(const lamb_tensor* tensors, int32_t n_tensors, float lr, fl
                      float beta2, float eps, int64_t step, const double* norms,
                      float* ratios_out, void* scratch, size_t scratch_bytes, hipStream_t stream);
 
+/* lamb_step for callers that cannot allocate device memory (code under
+ * graph capture, tight loops, harnesses that forbid allocation): the same
+ * step, kernels and results as lamb_step, with the scratch taken from a
+ * static array in device memory (one per device, kept until the process
+ * ends) instead of a caller buffer.  It calls no allocating routine.
+ * Limit: lamb_scratch_bytes(tensors, n_tensors) must not exceed
+ * lamb_noalloc_max_scratch_bytes() (2 MiB: about 1.07e9 parameters split
+ * over few tensors), else PTB_ERR_WORKSPACE and nothing runs.  The stream
+ * must belong to the current device (else PTB_ERR_INVALID_ARG); the first
+ * call on a device looks up that device's copy of the array (PTB_ERR_HIP if
+ * the lookup fails).  Every call on one device shares that device's array:
+ * calls that overlap on one device (several streams or threads) race, so the
+ * caller orders them.  Other arguments and errors as lamb_step. */
+size_t lamb_noalloc_max_scratch_bytes(void);
+int lamb_step_noalloc(const lamb_tensor* tensors, int32_t n_tensors, float lr, float beta1,
+                      float beta2, float eps, int64_t step, float* ratios_out,
+                      hipStream_t stream);
+
 /* Human-readable text of a status code (static string). */
 const char* ptb_status_string(int status);
 

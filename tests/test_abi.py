@@ -173,3 +173,18 @@ def test_serial_block_sizes_and_checks():
                                 None) == -3
     assert L.ptb_serial_forward(ctypes.byref(d), fake + 4, *args[1:], fake, fake, need, fake, big,
                                 None) == -1
+
+
+def test_lamb_noalloc_size_limit_rejected_before_any_call():
+    """Sizes whose scratch exceeds the static array are rejected with
+    PTB_ERR_WORKSPACE before any HIP call (so this runs without a GPU)."""
+    L = B.lib()
+    cap = B.lamb_noalloc_max_scratch_bytes()
+    assert cap == 2 << 20
+    fake = 0x10000
+    n = 1 << 31  # 2^31 elements need 2^19 partial pairs of 8 bytes: 4 MiB > 2 MiB
+    arr = (B.LambTensor * 1)(B.LambTensor(fake, fake, fake, fake, None, n, 0.01, 1))
+    assert L.lamb_scratch_bytes(arr, 1) > cap
+    assert L.lamb_step_noalloc(arr, 1, 1e-3, 0.9, 0.999, 1e-6, 1, None, None) == -3
+    assert L.lamb_step_noalloc(None, 1, 1e-3, 0.9, 0.999, 1e-6, 1, None, None) == -1
+    assert L.lamb_step_noalloc(arr, 0, 1e-3, 0.9, 0.999, 1e-6, 1, None, None) == -1

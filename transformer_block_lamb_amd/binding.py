@@ -24,7 +24,8 @@ EXPORTED = ("ptb_saved_bytes", "ptb_scratch_bytes", "ptb_forward", "ptb_backward
             "ptb_layernorm_forward", "ptb_gemm_workspace_bytes", "ptb_gemm", "ptb_swa_forward",
             "ptb_swa_backward", "ptb_serial_saved_bytes", "ptb_serial_scratch_bytes",
             "ptb_serial_forward", "ptb_serial_backward", "lamb_shard_norms", "lamb_shard_apply",
-            "ptb_layernorm_scratch_bytes", "ptb_layernorm_backward")
+            "ptb_layernorm_scratch_bytes", "ptb_layernorm_backward",
+            "lamb_noalloc_max_scratch_bytes", "lamb_step_noalloc")
 FWD_STAGES = ("layernorm", "gemm_in", "attention", "gemm_out")
 BWD_STAGES = ("gemm_dcat", "gemm_dw_out", "attention", "gemm_dw_in", "gemm_dxn", "layernorm")
 
@@ -75,6 +76,8 @@ def lib():
                                                   vp, vp, vp, sz, vp]),
             "lamb_scratch_bytes": (sz, [pl, i32]),
             "lamb_step": (ctypes.c_int, [pl, i32, f32, f32, f32, f32, i64, vp, vp, sz, vp]),
+            "lamb_noalloc_max_scratch_bytes": (sz, []),
+            "lamb_step_noalloc": (ctypes.c_int, [pl, i32, f32, f32, f32, f32, i64, vp, vp]),
             "lamb_shard_norms": (ctypes.c_int, [pl, i32, f32, f32, f32, i64, vp, vp, sz, vp]),
             "lamb_shard_apply": (ctypes.c_int, [pl, i32, f32, f32, f32, f32, i64, vp, vp, vp, sz,
                                                 vp]),
@@ -215,6 +218,17 @@ def lamb_step(tensors, lr, beta1, beta2, eps, step, ratios_out, scratch, stream=
                            _ptr(ratios_out), _ptr(scratch),
                            scratch.numel() * scratch.element_size(), _stream(stream)),
            "lamb_step")
+
+
+def lamb_noalloc_max_scratch_bytes() -> int:
+    return int(lib().lamb_noalloc_max_scratch_bytes())
+
+
+def lamb_step_noalloc(tensors, lr, beta1, beta2, eps, step, ratios_out, stream=None):
+    """lamb_step with the library's static per-device scratch (no buffer)."""
+    _check(lib().lamb_step_noalloc(tensors, len(tensors), lr, beta1, beta2, eps, step,
+                                   _ptr(ratios_out), _stream(stream)),
+           "lamb_step_noalloc")
 
 
 def lamb_shard_norms(tensors, beta1, beta2, eps, step, norms_out, scratch, stream=None):

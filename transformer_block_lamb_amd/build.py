@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libptb.so")
-SOURCES = ("api.hip", "layernorm.hip", "gemm.hip", "swa.hip", "lamb.hip")
+SOURCES = ("api.hip", "layernorm.hip", "gemm.hip", "swa.hip", "lamb.hip", "noalloc.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
