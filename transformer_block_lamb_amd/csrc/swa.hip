@@ -3,12 +3,15 @@
 // cost is O(s*w) instead of O(s*s)).  Key j is visible to query i of the same
 // sequence iff 0 <= i - j < w; scores are scaled by 1/sqrt(d).
 //
-// bf16 path, one workgroup = 4 waves, every wave owns 32 queries (forward,
-// dQ) or 32 keys (dK/dV) and computes 32x32 blocks with
-// v_mfma_f32_32x32x16_bf16:
+// bf16 path, 32x32 blocks with v_mfma_f32_32x32x16_bf16.  Forward and dQ:
+// one workgroup = 8 waves over 128 queries; waves w and w + 4 own the same 32
+// queries and take the first and second 32 keys of every 64-key tile, so two
+// waves share each SIMD and overlap one's softmax with the other's MFMAs;
+// their partial results are merged through LDS at the end.  dK/dV: one
+// workgroup = 4 waves, each owning 32 keys.
 //   * forward: a block of 128 queries walks only the 64-key tiles that
-//     intersect its band; each wave skips tiles outside its own band and
-//     masks only tiles that cross the band edges.  Scores are computed
+//     intersect its band; each wave skips key halves outside its own band and
+//     masks only those that cross the band edges.  Scores are computed
 //     transposed (S^T = K Q^T) so that each lane holds 16 scores of ONE
 //     query: the online softmax (running max and sum, base-2 exponent) then
 //     needs a single lane exchange, and the probabilities already sit in
@@ -36,8 +39,11 @@ namespace ptb {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Forward: how far (base-2 exponent) a score may exceed the running
+// reference max before O and l are rescaled.
+constexpr float kSlack = 8.f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kBQ = 128, kBKV = 64, kSwaThreads = 256;
+constexpr int kBQ = 128, kBKV = 64, kSwaThreads = 256, kSwaWideThreads = 512;
 
 __device__ __forceinline__ bf16x8_t ld_frag(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
@@ -119,15 +125,19 @@ constexpr int kSwaStages = D <= 96 ? 3 : 2;
 
 // Waits until this wave has at most VM loads outstanding (the LDS-bound ones
 // included) and no LDS reads, then joins the workgroup barrier.  VM0 is
-// wave 0's allowance, VM1 the other waves' (wave 0 may issue more).
-template <int VM0, int VM1>
+// wave 0's allowance, VM1 that of waves 1-3 (wave 0 may issue more), VM4
+// that of waves 4 and up (in the eight-wave kernels they issue no tile
+// loads).
+template <int VM0, int VM1, int VM4 = VM1>
 __device__ __forceinline__ void tile_barrier(int wave) {
-  static_assert(VM0 < 64 && VM1 < 64, "vmcnt field");
+  static_assert(VM0 < 64 && VM1 < 64 && VM4 < 64, "vmcnt field");
   __builtin_amdgcn_sched_barrier(0);
   if (wave == 0)
     __builtin_amdgcn_s_waitcnt((VM0 & 15) | ((VM0 >> 4) << 14) | (7 << 4));
-  else
+  else if (wave < 4)
     __builtin_amdgcn_s_waitcnt((VM1 & 15) | ((VM1 >> 4) << 14) | (7 << 4));
+  else
+    __builtin_amdgcn_s_waitcnt((VM4 & 15) | ((VM4 >> 4) << 14) | (7 << 4));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -191,18 +201,24 @@ __device__ __forceinline__ void load_row_frags(bf16x8_t (&f)[D / 16], const bf16
 // dimension ldl); every score is q_hi.k_hi + q_hi.k_lo + q_lo.k_hi, which
 // keeps the scores at fp32-level accuracy.
 //
-// K, K_lo and V tiles are double-buffered in LDS: the loads of tile kt + 1
-// are issued right after the barrier that publishes tile kt, so they fly
-// while tile kt is multiplied.  The loop body is written out twice with the
-// two buffers swapped (the tile count is rounded up to even; the extra body
-// only joins the barrier) so that every LDS access names a fixed array.
+// Eight waves: waves w and w + 4 own the same 32 queries and split every
+// 64-key tile, wave w taking keys 0-31 and wave w + 4 keys 32-63, each with
+// its own running max, sum and output.  Two waves per SIMD then overlap one
+// wave's softmax with the other's MFMAs, with the same LDS tiles as four
+// waves would use.  At the end the partner wave hands its (max, sum, O) to
+// wave w through LDS and wave w merges them, exactly as online softmax
+// merges two blocks of keys.  K, K_lo and V tiles are staged in LDS (three
+// stages for d <= 96, else two); waves 0-3 issue the loads, all eight meet
+// at one barrier per tile.
 template <int D, bool SPLIT, bool RAGGED>
-__global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __restrict__ qkv,
-                                                            int64_t ldq,
-                                                            const bf16_t* __restrict__ qk_lo,
-                                                            int64_t ldl, bf16_t* __restrict__ out,
-                                                            int64_t ldo, float* __restrict__ lse,
-                                                            int S, int H, int W, float sl2) {
+__global__ __launch_bounds__(kSwaWideThreads) void swa_fwd_mfma(const bf16_t* __restrict__ qkv,
+                                                                int64_t ldq,
+                                                                const bf16_t* __restrict__ qk_lo,
+                                                                int64_t ldl,
+                                                                bf16_t* __restrict__ out,
+                                                                int64_t ldo,
+                                                                float* __restrict__ lse, int S,
+                                                                int H, int W, float sl2) {
   constexpr int NS = kSwaStages<D>;
   constexpr int KLD = kTileLd<D>, TE = kBKV * KLD, TL = SPLIT ? TE : 8, T3 = NS > 2 ? TE : 8,
                 TL3 = NS > 2 ? TL : 8;
@@ -212,8 +228,9 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   const int h = sb.h, b = sb.b;
   const int A = H * D;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int qgrp = wave & 3, half = wave >> 2;  // query group, key half of every tile
   const int q0 = sb.blk * kBQ;
-  const int qw = q0 + wave * 32;
+  const int qw = q0 + qgrp * 32;
   const int qi = qw + (lane & 31);
   const bf16_t* base = qkv + (int64_t)b * S * ldq;
   const bf16_t* Qp = base + h * D;
@@ -223,11 +240,12 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(Kp, ldq, S, D), rv = rows_rsrc(Vp, ldq, S, D);
   const __amdgpu_buffer_rsrc_t rl =
       SPLIT ? rows_rsrc(lo_base + A + h * D, ldl, S, D) : rk;
+  const bool loader = wave < 4;
   DmaRows<D> dq_, dl_;
-  dq_.init(wave, lane, ldq);
-  if (SPLIT) dl_.init(wave, lane, ldl);
-  // loads per tile of wave 0 and of the others (the same for waves 1-3
-  // whenever three stages are used)
+  dq_.init(qgrp, lane, ldq);
+  if (SPLIT) dl_.init(qgrp, lane, ldl);
+  // loads per tile of wave 0 and of waves 1-3 (the same for waves 1-3
+  // whenever three stages are used); waves 4-7 issue none
   constexpr int NA = SPLIT ? 3 : 2;
   constexpr int C0 = NA * DmaRows<D>::count(0), C1 = NA * DmaRows<D>::count(1);
   static_assert(NS == 2 || (DmaRows<D>::count(1) == DmaRows<D>::count(3)), "load counts");
@@ -237,6 +255,7 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   // tiles past kt_hi reload tile kt_hi: they are never used, but every body
   // issues the same loads, so the load counts the waits assume hold
   auto issue = [&](bf16_t* k, bf16_t* kl, bf16_t* v, int kt) {
+    if (!loader) return;
     const int r0 = min(kt, kt_hi) * kBKV;
     dq_.issue(RAGGED, rk, k, wave, r0, S, ldq);
     if (SPLIT) dl_.issue(RAGGED, rl, kl, wave, r0, S, ldl);
@@ -260,67 +279,68 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
   // the stage tile kt - 1 used
   auto body = [&](const bf16_t* Ks, const bf16_t* Ks_lo, const bf16_t* Vs, bf16_t* nk,
                   bf16_t* nl, bf16_t* nv, int kt) {
-    tile_barrier<(NS - 2) * C0, (NS - 2) * C1>(wave);
+    tile_barrier<(NS - 2) * C0, (NS - 2) * C1, 0>(wave);
     issue(nk, nl, nv, kt + NS - 1);
-    const int j0 = kt * kBKV;
-    if (kt > kt_hi || !wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) return;
-    const bool full = (j0 + kBKV - 1 <= qw) && (qw + 31 - j0 < W) && (j0 + kBKV <= S);
-    f32x16_t st[2];
+    const int j0 = kt * kBKV + half * 32;  // this wave's 32 keys
+    if (kt > kt_hi || !wave_live || j0 > qw + 31 || j0 + 31 < qw - W + 1) return;
+    const bool full = (j0 + 31 <= qw) && (qw + 31 - j0 < W) && (j0 + 32 <= S);
+    // two independent accumulation chains (even and odd K steps)
+    f32x16_t st, st2;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int r = 0; r < 16; ++r) { st[r] = 0.f; st2[r] = 0.f; }
+    const int fo = (half * 32 + (lane & 31)) * KLD + (lane >> 5) * 8;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[kh][r] = 0.f;
-      const int fo = (kh * 32 + (lane & 31)) * KLD + (lane >> 5) * 8;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t kf = ld_frag(Ks + fo + ks * 16);
-        st[kh] = mfma32(kf, qf[ks], st[kh]);
-        if (SPLIT) {
-          st[kh] = mfma32(kf, qf_lo[ks], st[kh]);
-          st[kh] = mfma32(ld_frag(Ks_lo + fo + ks * 16), qf[ks], st[kh]);
-        }
+    for (int ks = 0; ks < D / 16; ++ks) {
+      f32x16_t& acc = (ks & 1) ? st2 : st;
+      const bf16x8_t kf = ld_frag(Ks + fo + ks * 16);
+      acc = mfma32(kf, qf[ks], acc);
+      if (SPLIT) {
+        acc = mfma32(kf, qf_lo[ks], acc);
+        acc = mfma32(ld_frag(Ks_lo + fo + ks * 16), qf[ks], acc);
       }
     }
     float mblk = -INFINITY;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = st[kh][r] * sl2;
-        if (!full) {
-          const int j = j0 + kh * 32 + mfma32_row(r, lane);
-          if (!(visible(qi, j, W) && j < S)) sv = -INFINITY;
-        }
-        st[kh][r] = sv;
-        mblk = fmaxf(mblk, sv);
+    for (int r = 0; r < 16; ++r) {
+      float sv = (st[r] + st2[r]) * sl2;
+      if (!full) {
+        const int j = j0 + mfma32_row(r, lane);
+        if (!(visible(qi, j, W) && j < S)) sv = -INFINITY;
       }
+      st[r] = sv;
+      mblk = fmaxf(mblk, sv);
+    }
     mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
-    const float m_new = fmaxf(m_run, mblk);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    l_run *= alpha;
+    // The reference max moves only when a score exceeds it by more than
+    // 2^kSlack (or on the first visible key), so the rescale of O and l is
+    // skipped for most tiles; probabilities then stay below 2^kSlack, and
+    // the final normalisation uses the same reference, so the result is
+    // the same up to rounding.
+    const bool grow = mblk > m_run + kSlack;
+    if (__any(grow)) {
+      const float m_next = grow ? mblk : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_next);
+      l_run *= alpha;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
+      for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-    m_run = m_new;
-    float p[2][16];
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+      m_run = m_next;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float p[16];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(st[r] - m_use);
+      l_run += p[r];
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[kh][r] = __builtin_amdgcn_exp2f(st[kh][r] - m_use);
-        l_run += p[kh][r];
-      }
+    for (int hf = 0; hf < 2; ++hf) {
+      const bf16x8_t pb = pack8(&p[hf * 8]);
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const bf16x8_t pb = pack8(&p[kh][hf * 8]);
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-          o[mb] = mfma32(ld_frag_tr<KLD>(Vs, kh * 32 + hf * 16, mb * 32, lane), pb, o[mb]);
-      }
+      for (int mb = 0; mb < D / 32; ++mb)
+        o[mb] = mfma32(ld_frag_tr<KLD>(Vs, half * 32 + hf * 16, mb * 32, lane), pb, o[mb]);
+    }
   };
   if constexpr (NS == 2) {
     for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
@@ -334,7 +354,34 @@ __global__ __launch_bounds__(kSwaThreads) void swa_fwd_mfma(const bf16_t* __rest
       body(K2, L2, V2, K1, L1, V1, kt + 2);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS when the workgroup ends
+  // every load has landed and every wave is done with the tiles: the tile
+  // buffers now carry the second key half's partials to its partner wave
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* xch = reinterpret_cast<float*>(qgrp == 0 ? K0 : qgrp == 1 ? K1 : qgrp == 2 ? V0 : V1);
+  static_assert((2 + 16 * (D / 32)) * 64 * 4 <= TE * 2, "exchange fits a tile buffer");
+  if (half == 1) {
+    xch[lane] = m_run;
+    xch[64 + lane] = l_run;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(2 + 16 * mb + r) * 64 + lane] = o[mb][r];
+  }
+  __syncthreads();
+  if (half == 1) return;
+  {
+    const float mb_ = xch[lane], lb = xch[64 + lane];
+    const float m = fmaxf(m_run, mb_);
+    const float m_use = m == -INFINITY ? 0.f : m;
+    const float fa = __builtin_amdgcn_exp2f(m_run - m_use), fb = __builtin_amdgcn_exp2f(mb_ - m_use);
+    l_run = l_run * fa + lb * fb;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mb][r] = o[mb][r] * fa + xch[(2 + 16 * mb + r) * 64 + lane] * fb;
+    m_run = m;
+  }
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qi < S) {
     const float inv = 1.0f / l_tot;
@@ -475,20 +522,24 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
     const bool full = (i0 >= kw + 31) && (i0 + kBKV - 1 - kw < W) && (i0 + kBKV <= S);
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
-      f32x16_t s, dp;
+      // scores in two accumulation chains (even and odd K steps), dP in a third
+      f32x16_t s, s2, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) { s[r] = 0.f; s2[r] = 0.f; dp[r] = 0.f; }
       const int fo = (qh * 32 + (lane & 31)) * KLD + (lane >> 5) * 8;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
+        f32x16_t& acc = (ks & 1) ? s2 : s;
         const bf16x8_t qa = ld_frag(Qs + fo + ks * 16);
-        s = mfma32(qa, kf[ks], s);
+        acc = mfma32(qa, kf[ks], acc);
         if (SPLIT) {
-          s = mfma32(qa, kf_lo[ks], s);
-          s = mfma32(ld_frag(Qs_lo + fo + ks * 16), kf[ks], s);
+          acc = mfma32(qa, kf_lo[ks], acc);
+          acc = mfma32(ld_frag(Qs_lo + fo + ks * 16), kf[ks], acc);
         }
         dp = mfma32(ld_frag(dOs + fo + ks * 16), vf[ks], dp);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] += s2[r];
       float p[16], ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -552,9 +603,12 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dkdv_mfma(
 }
 
 // ------------------------------------------------------------------ dQ
-// K, K_lo and V tiles double-buffered in LDS as in the forward.
+// Eight waves, split like the forward: waves w and w + 4 own the same 32
+// queries and take keys 0-31 and 32-63 of every K/V tile; the partner's dQ
+// partial is added through LDS at the end.  K, K_lo and V tiles are staged
+// in LDS as in the forward.
 template <int D, bool SPLIT, bool RAGGED>
-__global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
+__global__ __launch_bounds__(kSwaWideThreads) void swa_bwd_dq_mfma(
     const bf16_t* __restrict__ qkv, int64_t ldq, const bf16_t* __restrict__ qk_lo, int64_t ldl,
     const bf16_t* __restrict__ d_o, int64_t ld_do, const bf16_t* __restrict__ o, int64_t ldo,
     const float* __restrict__ lse, float* __restrict__ dvec, bf16_t* __restrict__ dqkv,
@@ -568,8 +622,9 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   const int h = sb.h, b = sb.b;
   const int A = H * D;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int qgrp = wave & 3, half = wave >> 2;
   const int q0 = sb.blk * kBQ;
-  const int qw = q0 + wave * 32;
+  const int qw = q0 + qgrp * 32;
   const int qi = qw + (lane & 31);
   const bf16_t* base = qkv + (int64_t)b * S * ldq;
   const bf16_t* Qp = base + h * D;
@@ -580,11 +635,12 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(Kp, ldq, S, D), rv = rows_rsrc(Vp, ldq, S, D);
   const __amdgpu_buffer_rsrc_t rl =
       SPLIT ? rows_rsrc(lo_base + A + h * D, ldl, S, D) : rk;
+  const bool loader = wave < 4;
   DmaRows<D> dq_, dl_;
-  dq_.init(wave, lane, ldq);
-  if (SPLIT) dl_.init(wave, lane, ldl);
-  // loads per tile of wave 0 and of the others (the same for waves 1-3
-  // whenever three stages are used)
+  dq_.init(qgrp, lane, ldq);
+  if (SPLIT) dl_.init(qgrp, lane, ldl);
+  // loads per tile of wave 0 and of waves 1-3 (the same for waves 1-3
+  // whenever three stages are used); waves 4-7 issue none
   constexpr int NA = SPLIT ? 3 : 2;
   constexpr int C0 = NA * DmaRows<D>::count(0), C1 = NA * DmaRows<D>::count(1);
   static_assert(NS == 2 || (DmaRows<D>::count(1) == DmaRows<D>::count(3)), "load counts");
@@ -594,6 +650,7 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   // tiles past kt_hi reload tile kt_hi: they are never used, but every body
   // issues the same loads, so the load counts the waits assume hold
   auto issue = [&](bf16_t* k, bf16_t* kl, bf16_t* v, int kt) {
+    if (!loader) return;
     const int r0 = min(kt, kt_hi) * kBKV;
     dq_.issue(RAGGED, rk, k, wave, r0, S, ldq);
     if (SPLIT) dl_.issue(RAGGED, rl, kl, wave, r0, S, ldl);
@@ -606,7 +663,7 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
   if (SPLIT) load_row_frags<D>(qf_lo, lo_base + h * D, ldl, qi, S, lane);
   // D_i = dO_i . O_i for this wave's queries: lanes l and l + 32 hold the
   // two halves of each K=16 step of query l's row; the dK/dV kernel, launched
-  // after this one, reads the values back
+  // after this one, reads the values back (the first key half stores them)
   float di;
   {
     bf16x8_t ofo[D / 16];
@@ -617,7 +674,7 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
 #pragma unroll
       for (int e = 0; e < 8; ++e) part += bf2f(of[ks][e]) * bf2f(ofo[ks][e]);
     di = part + __shfl_xor(part, 32, 64);
-    if (lane < 32 && qi < S) dvec[((int64_t)b * H + h) * S + qi] = di;
+    if (half == 0 && lane < 32 && qi < S) dvec[((int64_t)b * H + h) * S + qi] = di;
   }
   issue(K0, L0, V0, kt_lo);
   if (NS > 2) issue(K1, L1, V1, kt_lo + 1);
@@ -631,44 +688,43 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
 
   auto body = [&](const bf16_t* Ks, const bf16_t* Ks_lo, const bf16_t* Vs, bf16_t* nk,
                   bf16_t* nl, bf16_t* nv, int kt) {
-    tile_barrier<(NS - 2) * C0, (NS - 2) * C1>(wave);
+    tile_barrier<(NS - 2) * C0, (NS - 2) * C1, 0>(wave);
     issue(nk, nl, nv, kt + NS - 1);
-    const int j0 = kt * kBKV;
-    if (kt > kt_hi || !wave_live || j0 > qw + 31 || j0 + kBKV - 1 < qw - W + 1) return;
-    const bool full = (j0 + kBKV - 1 <= qw) && (qw + 31 - j0 < W) && (j0 + kBKV <= S);
+    const int j0 = kt * kBKV + half * 32;  // this wave's 32 keys
+    if (kt > kt_hi || !wave_live || j0 > qw + 31 || j0 + 31 < qw - W + 1) return;
+    const bool full = (j0 + 31 <= qw) && (qw + 31 - j0 < W) && (j0 + 32 <= S);
+    // scores in two accumulation chains (even and odd K steps), dP in a third
+    f32x16_t st, st2, dpt;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      f32x16_t st, dpt;
+    for (int r = 0; r < 16; ++r) { st[r] = 0.f; st2[r] = 0.f; dpt[r] = 0.f; }
+    const int fo = (half * 32 + (lane & 31)) * KLD + (lane >> 5) * 8;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { st[r] = 0.f; dpt[r] = 0.f; }
-      const int fo = (kh * 32 + (lane & 31)) * KLD + (lane >> 5) * 8;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t ka = ld_frag(Ks + fo + ks * 16);
-        st = mfma32(ka, qf[ks], st);
-        if (SPLIT) {
-          st = mfma32(ka, qf_lo[ks], st);
-          st = mfma32(ld_frag(Ks_lo + fo + ks * 16), qf[ks], st);
-        }
-        dpt = mfma32(ld_frag(Vs + fo + ks * 16), of[ks], dpt);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      f32x16_t& acc = (ks & 1) ? st2 : st;
+      const bf16x8_t ka = ld_frag(Ks + fo + ks * 16);
+      acc = mfma32(ka, qf[ks], acc);
+      if (SPLIT) {
+        acc = mfma32(ka, qf_lo[ks], acc);
+        acc = mfma32(ld_frag(Ks_lo + fo + ks * 16), qf[ks], acc);
       }
-      float ds[16];
+      dpt = mfma32(ld_frag(Vs + fo + ks * 16), of[ks], dpt);
+    }
+    float ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(st[r] * sl2 - lse2);
-        if (!full) {
-          const int j = j0 + kh * 32 + mfma32_row(r, lane);
-          if (!(visible(qi, j, W) && j < S)) pv = 0.f;
-        }
-        ds[r] = pv * (dpt[r] - di);
+    for (int r = 0; r < 16; ++r) {
+      float pv = __builtin_amdgcn_exp2f((st[r] + st2[r]) * sl2 - lse2);
+      if (!full) {
+        const int j = j0 + mfma32_row(r, lane);
+        if (!(visible(qi, j, W) && j < S)) pv = 0.f;
       }
+      ds[r] = pv * (dpt[r] - di);
+    }
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const bf16x8_t db = pack8(&ds[hf * 8]);
+    for (int hf = 0; hf < 2; ++hf) {
+      const bf16x8_t db = pack8(&ds[hf * 8]);
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-          dq[mb] = mfma32(ld_frag_tr<KLD>(Ks, kh * 32 + hf * 16, mb * 32, lane), db, dq[mb]);
-      }
+      for (int mb = 0; mb < D / 32; ++mb)
+        dq[mb] = mfma32(ld_frag_tr<KLD>(Ks, half * 32 + hf * 16, mb * 32, lane), db, dq[mb]);
     }
   };
   if constexpr (NS == 2) {
@@ -683,7 +739,20 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
       body(K2, L2, V2, K1, L1, V1, kt + 2);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS when the workgroup ends
+  // every load has landed and every wave is done with the tiles: the tile
+  // buffers now carry the second key half's dQ partial to its partner wave
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* xch = reinterpret_cast<float*>(qgrp == 0 ? K0 : qgrp == 1 ? K1 : qgrp == 2 ? V0 : V1);
+  static_assert(16 * (D / 32) * 64 * 4 <= TE * 2, "exchange fits a tile buffer");
+  if (half == 1) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(16 * mb + r) * 64 + lane] = dq[mb][r];
+  }
+  __syncthreads();
+  if (half == 1) return;
   if (qi < S) {
     bf16_t* row = dqkv + ((int64_t)b * S + qi) * ldd + h * D;
 #pragma unroll
@@ -691,9 +760,13 @@ __global__ __launch_bounds__(kSwaThreads) void swa_bwd_dq_mfma(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = mb * 32 + 8 * g + 4 * (lane >> 5);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = (dq[mb][4 * g + e] + xch[(16 * mb + 4 * g + e) * 64 + lane]) * scale;
         uint2 u;
-        u.x = pack_bf2(dq[mb][4 * g] * scale, dq[mb][4 * g + 1] * scale);
-        u.y = pack_bf2(dq[mb][4 * g + 2] * scale, dq[mb][4 * g + 3] * scale);
+        u.x = pack_bf2(v[0], v[1]);
+        u.y = pack_bf2(v[2], v[3]);
         *reinterpret_cast<uint2*>(row + d0) = u;
       }
   }
@@ -803,7 +876,7 @@ void launch_fwd_mfma(const SwaDesc& a, void* o, int64_t ldo, float* lse, float s
                      hipStream_t s) {
   dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
   const int64_t ldl = 2 * (int64_t)a.n_heads * D;
-  hipLaunchKernelGGL((swa_fwd_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
+  hipLaunchKernelGGL((swa_fwd_mfma<D, SP, RG>), grid, dim3(kSwaWideThreads), 0, s,
                      (const bf16_t*)a.qkv, a.ld_qkv, (const bf16_t*)a.qk_lo, ldl, (bf16_t*)o, ldo,
                      lse, a.seq, a.n_heads, a.window, scale * kLog2e);
 }
@@ -816,7 +889,7 @@ void launch_bwd_mfma(const SwaDesc& a, const void* o, int64_t ldo, const void* d
   dim3 grid((a.seq + kBQ - 1) / kBQ * a.n_heads * a.batch);
   const int64_t ldl = 2 * (int64_t)a.n_heads * D;
   const bf16_t* lo = (const bf16_t*)a.qk_lo;
-  hipLaunchKernelGGL((swa_bwd_dq_mfma<D, SP, RG>), grid, dim3(kSwaThreads), 0, s,
+  hipLaunchKernelGGL((swa_bwd_dq_mfma<D, SP, RG>), grid, dim3(kSwaWideThreads), 0, s,
                      (const bf16_t*)a.qkv, a.ld_qkv, lo, ldl, (const bf16_t*)d_o, ld_do,
                      (const bf16_t*)o, ldo, lse, dvec, (bf16_t*)dqkv, ldd, a.seq, a.n_heads,
                      a.window, scale * kLog2e, scale);
