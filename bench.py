@@ -50,6 +50,9 @@ def parse():
                    help="skip timing the serial pre-LN block on the same workload")
     p.add_argument("--no-lamb-shard", action="store_true",
                    help="skip timing one data-parallel rank's sharded LAMB")
+    p.add_argument("--no-extra-configs", action="store_true",
+                   help="skip the forward + backward timings of the other workloads "
+                        "(175b_w2048, small, 530b_w512)")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run one plain device-to-device copy of MIB MiB and exit (the "
@@ -110,6 +113,126 @@ def lamb_bytes(params):
         total += n * (4 + g + 4 + 4 + 4 + 4)            # pass A
         total += n * (12 + 4 + (2 if p.get("w_bf16") is not None else 0))  # pass B
     return total
+
+
+def lamb_bytes_headline(params):
+    """The two-pass exact minimum of the step without the bf16 weight copy:
+    38 B/param with bf16 gradients (pass A 22 B, pass B 16 B)."""
+    total = 0
+    for p in params:
+        n = p["w"].numel()
+        total += n * (4 + p["g"].element_size() + 4 + 4 + 4 + 4) + n * (12 + 4)
+    return total
+
+
+def ln_bytes(cfg):
+    """HBM bytes the two LayerNorm stages must move (activations in the layer
+    dtype, statistics and LN parameters in fp32).
+    forward : read x; write xn, and for bf16 the residual xn - bf16(xn) that
+              the compensated q/k pass reads; write mean, rstd
+    backward: read x, dxn (and dy when the residual is on), mean, rstd,
+              gamma; write dx, dgamma, dbeta
+    The backward's per-workgroup partial column sums (written, then read by
+    the fixed-order reduction) are extra traffic, reported separately."""
+    T, h = cfg.tokens, cfg.hidden
+    e = 2 if cfg.dtype == "bf16" else 4
+    fwd = T * h * e + T * h * e + (T * h * 2 if e == 2 else 0) + 8 * T + 8 * h
+    bwd = T * h * e * (3 if cfg.add_residual else 2) + T * h * e + 8 * T + 4 * h + 8 * h
+    rows_per_block = 8
+    nblk = -(-T // rows_per_block)
+    partials = 2 * (2 * nblk * h * 4)
+    return {"fwd": fwd, "bwd": bwd, "bwd_partials": partials}
+
+
+def time_stages(shard, nfwd, nbwd, steps):
+    """Mean milliseconds of each stage over `steps` forward + backward passes
+    through the stage entry points, with a HIP event before each stage on the
+    stream the library launches on (torch's current stream)."""
+    import numpy as np
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nfwd + nbwd + 1)]
+          for _ in range(steps)]
+    for k in range(steps):
+        i = 0
+        for s in range(nfwd):
+            ev[k][i].record(); i += 1
+            shard.forward_stage(s)
+        for s in range(nbwd):
+            ev[k][i].record(); i += 1
+            shard.backward_stage(s)
+        ev[k][i].record()
+    torch.cuda.synchronize()
+    return [float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)]))
+            for i in range(nfwd + nbwd)]
+
+
+def roofline_for(cfg, per_stage):
+    """The dominant stage (a GEMM) against the dense bf16 MFMA peak."""
+    flops = stage_flops(cfg)
+    dom = max((n for n in per_stage if n in flops and n != "lamb"), key=lambda n: per_stage[n])
+    achieved = flops[dom] / (per_stage[dom] * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+            "frac": round(achieved / (PEAK_BF16 / 1e12), 4),
+            "traffic": traffic_for(dom) if cfg.name == "175b_w512" else None,
+            "flop_per_launch": flops[dom], "ms_per_launch": round(per_stage[dom], 4)}
+
+
+def ln_rates(cfg, per_stage):
+    lb = ln_bytes(cfg)
+    f = lb["fwd"] / (per_stage["fwd.layernorm"] * 1e-3)
+    b = lb["bwd"] / (per_stage["bwd.layernorm"] * 1e-3)
+    m = (lb["bwd"] + lb["bwd_partials"]) / (per_stage["bwd.layernorm"] * 1e-3)
+    return {"fwd_bytes": lb["fwd"], "fwd_gbps": round(f / 1e9, 1),
+            "fwd_hbm_frac": round(f / PEAK_HBM, 4),
+            "bwd_bytes": lb["bwd"], "bwd_gbps": round(b / 1e9, 1),
+            "bwd_hbm_frac": round(b / PEAK_HBM, 4),
+            "bwd_with_partials_gbps": round(m / 1e9, 1)}
+
+
+def time_config(name, args):
+    """Forward + backward of another workload: whole calls timed with events,
+    then the per-stage breakdown, the dominant stage's roofline and the
+    LayerNorm rates."""
+    import numpy as np
+    import torch
+    from transformer_block_lamb_amd import binding as B
+    from transformer_block_lamb_amd.device import PtbShard
+    from transformer_block_lamb_amd.synth import CONFIGS, ptb_inputs
+    cfg = CONFIGS[name]
+    shard = PtbShard(cfg, ptb_inputs(cfg))
+    for _ in range(args.warmup):
+        shard.forward()
+        shard.backward()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record()
+        shard.forward()
+        ev[k][1].record()
+        shard.backward()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    st = time_stages(shard, len(B.FWD_STAGES), len(B.BWD_STAGES), args.steps)
+    names = [f"fwd.{n}" for n in B.FWD_STAGES] + [f"bwd.{n}" for n in B.BWD_STAGES]
+    per_stage = dict(zip(names, st))
+    mf = model_flops(cfg)
+    ex = sum(stage_flops(cfg).values())
+    out = {"workload": f"{cfg.name}: batch {cfg.batch}, seq {cfg.seq}, hidden {cfg.hidden}, "
+                       f"{cfg.n_heads} heads x {cfg.head_dim}, ffn {cfg.ffn}, window "
+                       f"{cfg.window}, {cfg.dtype}",
+           "fwd_ms": round(f, 4), "bwd_ms": round(b, 4),
+           "model_tflops": round(mf / ((f + b) * 1e-3) / 1e12, 2),
+           "mfu": round(mf / ((f + b) * 1e-3) / PEAK_BF16, 4),
+           "executed_tflops": round(ex / ((f + b) * 1e-3) / 1e12, 2),
+           "stages_ms": {n: round(v, 4) for n, v in per_stage.items()},
+           "roofline": roofline_for(cfg, per_stage),
+           "layernorm": ln_rates(cfg, per_stage)}
+    del shard
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_serial(cfg, inputs, args, ptb_ms):
@@ -273,18 +396,6 @@ def main():
         if events is not None:
             events[3].record()
 
-    def staged(events):
-        """The same forward and backward through the stage entry points, with
-        an event before each stage (the per-stage breakdown)."""
-        k = 0
-        for s in range(len(B.FWD_STAGES)):
-            events[k].record(); k += 1
-            shard.forward_stage(s)
-        for s in range(len(B.BWD_STAGES)):
-            events[k].record(); k += 1
-            shard.backward_stage(s)
-        events[k].record()
-
     for it in range(1, args.warmup + 1):
         step(it)
     torch.cuda.synchronize()
@@ -306,12 +417,8 @@ def main():
     # stage entry points (the events between stages add about 1.5 us each,
     # so these stages sum to slightly more than fwd_ms + bwd_ms)
     nfb = len(B.FWD_STAGES) + len(B.BWD_STAGES)
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(nfb + 1)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        staged(sev[k])
-    torch.cuda.synchronize()
-    per_stage = {n: float(np.mean([sev[k][i].elapsed_time(sev[k][i + 1]) for k in range(args.steps)]))
-                 for i, n in enumerate(names[:nfb])}
+    per_stage = dict(zip(names[:nfb], time_stages(shard, len(B.FWD_STAGES), len(B.BWD_STAGES),
+                                                  args.steps)))
     per_stage["lamb"] = lamb_ms
 
     serial = None
@@ -324,14 +431,13 @@ def main():
     value = mflops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
     executed = sum(flops.values()) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
     lb = lamb_bytes(params)
-
-    dom = max((n for n in names if n != "lamb"), key=lambda n: per_stage[n])
-    achieved = flops[dom] / (per_stage[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": round(achieved / (PEAK_BF16 / 1e12), 4),
-                "traffic": traffic_for(dom), "flop_per_launch": flops[dom],
-                "ms_per_launch": round(per_stage[dom], 4)}
+    lb38 = lamb_bytes_headline(params)
+    roofline = roofline_for(cfg, {n: v for n, v in per_stage.items() if n != "lamb"})
+    extra = {}
+    if not args.no_extra_configs:
+        for name in ("175b_w2048", "small", "530b_w512"):
+            if name != cfg.name:
+                extra[name] = time_config(name, args)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -346,14 +452,22 @@ def main():
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "lamb_ms": round(lamb_ms, 4),
         "fwd_bwd_ms_median": round(float(np.median(fb_each)), 4),
         "fwd_bwd_ms_min": round(float(np.min(fb_each)), 4),
-        "lamb_gbps": round(lb / (lamb_ms * 1e-3) / 1e9, 1),
-        "lamb_hbm_frac": round(lb / (lamb_ms * 1e-3) / PEAK_HBM, 4),
-        "lamb_bytes": lb,
+        # headline accounting: 38 B/param (two-pass exact minimum, bf16 g)
+        "lamb_gbps": round(lb38 / (lamb_ms * 1e-3) / 1e9, 1),
+        "lamb_hbm_frac": round(lb38 / (lamb_ms * 1e-3) / PEAK_HBM, 4),
+        "lamb_bytes": lb38,
+        # including the bf16 weight copy pass B also writes (40 B/param)
+        "lamb_with_copy_gbps": round(lb / (lamb_ms * 1e-3) / 1e9, 1),
+        "lamb_with_copy_hbm_frac": round(lb / (lamb_ms * 1e-3) / PEAK_HBM, 4),
+        "lamb_with_copy_bytes": lb,
+        "layernorm": ln_rates(cfg, per_stage),
         "executed_tflops": round(executed, 2),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4),
         "stages_ms": {n: round(v, 4) for n, v in per_stage.items()},
         "roofline": roofline,
     }
+    if extra:
+        out["configs"] = extra
     if lamb_shard is not None:
         out["lamb_zero2_rank"] = lamb_shard
     if serial is not None:

@@ -169,33 +169,54 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(
   }
 }
 
-// Forward: one workgroup per row.
+// Forward: each workgroup normalises kFwdRows consecutive rows; the next
+// row's loads are issued before the current row is reduced and stored, so
+// one row's stores overlap the next row's loads.
+constexpr int kFwdRows = 2;
+template <typename T, int NV>
+__device__ __forceinline__ void ln_fwd_row(const Raw8<T> (&raw)[NV], const float* __restrict__ gamma,
+                                           const float* __restrict__ beta, float eps, int width,
+                                           int row, T* __restrict__ xn, T* __restrict__ xn_lo,
+                                           float* __restrict__ mean_out,
+                                           float* __restrict__ rstd_out, float* red);
+
 template <typename T, int NV>
 __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict__ x,
                                                             const float* __restrict__ gamma,
                                                             const float* __restrict__ beta,
-                                                            float eps, int width,
+                                                            float eps, int rows, int width,
                                                             T* __restrict__ xn,
                                                             T* __restrict__ xn_lo,
                                                             float* __restrict__ mean_out,
                                                             float* __restrict__ rstd_out) {
   __shared__ float red[kLnWaves];
-  const int row = blockIdx.x;
   const int nvec = width >> 3;
-  const T* xr = x + (int64_t)row * width;
+  const int r0 = blockIdx.x * kFwdRows;
+  const int rend = min(rows, r0 + kFwdRows);
+  Raw8<T> cur[NV], nxt[NV];
+  load_raw<T, NV>(x + (int64_t)r0 * width, nvec, cur);
+  for (int row = r0; row < rend; ++row) {  // uniform over the block
+    if (row + 1 < rend) load_raw<T, NV>(x + (int64_t)(row + 1) * width, nvec, nxt);
+    ln_fwd_row<T, NV>(cur, gamma, beta, eps, width, row, xn, xn_lo, mean_out, rstd_out, red);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
+  }
+}
+
+template <typename T, int NV>
+__device__ __forceinline__ void ln_fwd_row(const Raw8<T> (&raw)[NV], const float* __restrict__ gamma,
+                                           const float* __restrict__ beta, float eps, int width,
+                                           int row, T* __restrict__ xn, T* __restrict__ xn_lo,
+                                           float* __restrict__ mean_out,
+                                           float* __restrict__ rstd_out, float* red) {
+  const int nvec = width >> 3;
   float v[NV][8];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int vi = threadIdx.x + kLnThreads * i;
-    if (vi < nvec) {
-      Vec8<T>::load(xr + vi * 8, v[i]);
+    raw[i].get(v[i]);  // zeros past the width
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[i][e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-    }
+    for (int e = 0; e < 8; ++e) s += v[i][e];
   }
   const float inv_w = 1.0f / (float)width;
   const float mean = block_sum<kLnWaves>(s, red) * inv_w;
@@ -348,8 +369,9 @@ __global__ __launch_bounds__(kRedCols * kRedGroups) void ln_bwd_reduce_kernel(
 template <typename T, int NV>
 hipError_t fwd_nv(const void* x, const float* g, const float* b, float eps, int rows, int width,
                   void* xn, void* xn_lo, float* mean, float* rstd, hipStream_t s) {
-  hipLaunchKernelGGL((ln_fwd_kernel<T, NV>), dim3(rows), dim3(kLnThreads), 0, s,
-                     (const T*)x, g, b, eps, width, (T*)xn, (T*)xn_lo, mean, rstd);
+  hipLaunchKernelGGL((ln_fwd_kernel<T, NV>), dim3((rows + kFwdRows - 1) / kFwdRows),
+                     dim3(kLnThreads), 0, s, (const T*)x, g, b, eps, rows, width, (T*)xn,
+                     (T*)xn_lo, mean, rstd);
   return hipGetLastError();
 }
 
