@@ -50,6 +50,9 @@ def parse():
                    help="skip timing the serial pre-LN block on the same workload")
     p.add_argument("--no-lamb-shard", action="store_true",
                    help="skip timing one data-parallel rank's sharded LAMB")
+    p.add_argument("--cpu-baseline-all", action="store_true",
+                   help="also time the fp64 CPU oracle's forward + backward on every other "
+                        "workload (minutes of host time; off by default)")
     p.add_argument("--no-extra-configs", action="store_true",
                    help="skip the forward + backward timings of the other workloads "
                         "(175b_w2048, small, 530b_w512)")
@@ -476,6 +479,14 @@ def main():
         out["serial"] = serial
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inputs, mflops)
+        if args.cpu_baseline_all:
+            from transformer_block_lamb_amd.synth import ptb_inputs as _inputs
+            per = {}
+            for name in ("tiny", "small", "175b_w2048", "530b_w512"):
+                c = CONFIGS[name]
+                per[name] = cpu_baseline(c, _inputs(c), model_flops(c))
+                print(f"cpu baseline {name}: {per[name]['seconds']} s", file=sys.stderr, flush=True)
+            out["cpu_baseline"]["per_config"] = per
     line = json.dumps(out)
     print(line, flush=True)
     if args.out:

@@ -156,6 +156,29 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// Two independent sums over a workgroup at once (one LDS exchange, two
+// barriers instead of four); `red` is LDS of >= 2 * NWAVES floats.
+template <int NWAVES>
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[wid] = a;
+    red[NWAVES + wid] = b;
+  }
+  __syncthreads();
+  float ta = 0.f, tb = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) {
+    ta += red[i];
+    tb += red[NWAVES + i];
+  }
+  __syncthreads();
+  a = ta;
+  b = tb;
+}
+
 // ---------------------------------------------------------------- GeLU
 // erf by the rational approximation of Abramowitz & Stegun, Handbook of
 // Mathematical Functions, formula 7.1.26 (absolute error <= 1.5e-7), written

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(
     const float* __restrict__ rstd, const T* __restrict__ dxn, const T* __restrict__ dy,
     T* __restrict__ dx, float* __restrict__ gpart, float* __restrict__ bpart, int rows,
     int width) {
-  __shared__ float red[kLnWaves];
+  __shared__ float red[2 * kLnWaves];
   const int nvec = width >> 3;
   const int r0 = blockIdx.x * kRowsPerBlock;
   const int rend = min(rows, r0 + kRowsPerBlock);
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(
         ab[i][e] += dv[e];
       }
     }
-    const float m1 = block_sum<kLnWaves>(s1, red) * inv_w;
-    const float m2 = block_sum<kLnWaves>(s2, red) * inv_w;
+    block_sum2<kLnWaves>(s1, s2, red);
+    const float m1 = s1 * inv_w, m2 = s2 * inv_w;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + kLnThreads * i;
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_plain_kernel(
     const float* __restrict__ rstd, const T* __restrict__ dxn, const T* __restrict__ dy,
     T* __restrict__ dx, float* __restrict__ gpart, float* __restrict__ bpart, int rows,
     int width) {
-  __shared__ float red[kLnWaves];
+  __shared__ float red[2 * kLnWaves];
   const int nvec = width >> 3;
   const int r0 = blockIdx.x * kRowsPerBlock;
   const float inv_w = 1.0f / (float)width;
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_plain_kernel(
         for (int e = 0; e < 8; ++e) { xh[i][e] = 0.f; dxh[i][e] = 0.f; }
       }
     }
-    const float m1 = block_sum<kLnWaves>(s1, red) * inv_w;
-    const float m2 = block_sum<kLnWaves>(s2, red) * inv_w;
+    block_sum2<kLnWaves>(s1, s2, red);
+    const float m1 = s1 * inv_w, m2 = s2 * inv_w;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + kLnThreads * i;
