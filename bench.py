@@ -424,6 +424,8 @@ def main():
                                                   args.steps)))
     per_stage["lamb"] = lamb_ms
 
+    print(f"{cfg.name}: fwd+bwd {fwd_ms + bwd_ms:.4f} ms, lamb {lamb_ms:.4f} ms", file=sys.stderr,
+          flush=True)
     serial = None
     if not args.no_serial:
         serial = time_serial(cfg, inputs, args, fwd_ms + bwd_ms)
@@ -440,6 +442,7 @@ def main():
     if not args.no_extra_configs:
         for name in ("175b_w2048", "small", "530b_w512"):
             if name != cfg.name:
+                print(f"timing {name}", file=sys.stderr, flush=True)
                 extra[name] = time_config(name, args)
 
     out = {
