@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import shutil
 import subprocess
 import sys
 
@@ -36,6 +37,20 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_launch_stubs(lib: str) -> None:
+    """Refuse a library that references a kernel's host launch stub without
+    defining it: hipcc can silently drop the stub of a kernel instance whose
+    host-side instantiation fails, and the library would then load only
+    until the first call reaches that symbol."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    r = subprocess.run([nm, "-u", lib], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the library:\n  " + "\n  ".join(missing))
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
@@ -45,6 +60,7 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    _check_launch_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
