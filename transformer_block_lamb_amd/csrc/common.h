@@ -183,12 +183,14 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
 // erf by the rational approximation of Abramowitz & Stegun, Handbook of
 // Mathematical Functions, formula 7.1.26 (absolute error <= 1.5e-7), written
 // inline so that epilogues holding hundreds of accumulators make no calls.
+// The reciprocal and the exponential use the hardware approximations
+// (v_rcp_f32, v_exp_f32: about one ulp), far inside the formula's own error.
 __device__ __forceinline__ float erf_as(float x) {
   const float ax = fabsf(x);
-  const float t = 1.0f / (1.0f + 0.3275911f * ax);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
   const float poly =
       t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
-  const float y = 1.0f - poly * __expf(-ax * ax);
+  const float y = 1.0f - poly * __builtin_amdgcn_exp2f(-1.4426950408889634f * ax * ax);
   return copysignf(y, x);
 }
 // Exact GeLU f * Phi(f) and its derivative Phi(f) + f * phi(f).
@@ -197,7 +199,7 @@ __device__ __forceinline__ float gelu_f(float f) {
 }
 __device__ __forceinline__ float gelu_grad_f(float f) {
   const float cdf = 0.5f * (1.0f + erf_as(f * 0.70710678118654752f));
-  const float pdf = 0.39894228040143268f * __expf(-0.5f * f * f);
+  const float pdf = 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * f * f);
   return cdf + f * pdf;
 }
 
