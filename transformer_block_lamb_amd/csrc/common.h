@@ -197,10 +197,16 @@ __device__ __forceinline__ float erf_as(float x) {
 __device__ __forceinline__ float gelu_f(float f) {
   return 0.5f * f * (1.0f + erf_as(f * 0.70710678118654752f));
 }
+// (The derivative evaluates exp(-f^2 / 2) once: the erf formula at
+// f / sqrt(2) and the normal density both use it.)
 __device__ __forceinline__ float gelu_grad_f(float f) {
-  const float cdf = 0.5f * (1.0f + erf_as(f * 0.70710678118654752f));
-  const float pdf = 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * f * f);
-  return cdf + f * pdf;
+  const float x = f * 0.70710678118654752f, ax = fabsf(x);
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * ax * ax);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float erf = copysignf(1.0f - poly * e, x);
+  return 0.5f * (1.0f + erf) + f * (0.39894228040143268f * e);
 }
 
 }  // namespace ptb
