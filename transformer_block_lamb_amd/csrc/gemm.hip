@@ -597,11 +597,7 @@ __device__ __forceinline__ void wait_barrier() {
 // lane).  A lane first gathers its four chunks and issues the epilogue's own
 // loads for all of them (pre8), then combines and stores (store8p), so those
 // loads are in flight together instead of one after another.  Every lane
-// issues 16-byte stores.  A wave touches only its own staging area and the
-// LDS operations of one wave complete in order, so a strip needs no
-// workgroup barrier; the caller meets the workgroup once after its last
-// strip, before the next segment's loads reuse the slots that hold the
-// staging areas.
+// issues 16-byte stores.  Contains two workgroup barriers.
 constexpr int kStageRow = 36, kStageBlk = 1216;
 template <class Epi>
 __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* stage, int row0,
@@ -612,6 +608,7 @@ __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* st
 #pragma unroll
     for (int r = 0; r < 16; ++r) blk[mfma32_row(r, lane) * kStageRow + (lane & 31)] = a[j][r];
   }
+  __syncthreads();
   constexpr int kChunks = 32 * 8 / 64;  // 8-column chunks of the 32x64 strip per lane
   float v[kChunks][8];
   typename Epi::Pre pre[kChunks];
@@ -634,6 +631,7 @@ __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* st
     const int row = row0 + rr, col = col0 + j * 32 + c8;
     if (row < M && col < N) epi.store8p(row, col, v[q], pre[q], N);
   }
+  __syncthreads();
 }
 
 // Offset (floats) of this lane's accumulators acc[i][j][4 r4 .. 4 r4 + 3] in
@@ -803,7 +801,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         epilogue_strip(acc[i], stage, m0 + wm * 128 + i * 32, n0 + wn * 64, lane, g.M, g.N, epi);
-      __syncthreads();  // staging reads done before the next segment's loads
     } else {
       // Partials move with device-scope (sc1) buffer stores and loads, which
       // other XCDs see without a writeback or invalidation of the whole L2.
@@ -864,7 +861,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
           }
           epilogue_strip(a, stage, m0 + wm * 128 + i * 32, n0 + wn * 64, lane, g.M, g.N, epi);
         }
-        __syncthreads();  // staging reads done before the next segment's loads
       }
     }
   }
