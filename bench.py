@@ -327,6 +327,19 @@ def cpu_baseline(cfg, inputs, mflops):
                       f"in fp64 numpy, model FLOPs 6*N*T over its wall time"}
 
 
+# The sources the GEMM kernels are compiled from: counters taken from any
+# other version of them no longer describe the kernels that run.
+GEMM_SOURCES = ("gemm.hip", "common.h", "kernels.h")
+
+
+def gemm_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "transformer_block_lamb_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_for(kernel_stage):
     """HBM bytes per launch of the dominant stage from the committed counter
     summary, or None when absent or taken from a different kernel source."""
@@ -335,10 +348,7 @@ def traffic_for(kernel_stage):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    import hashlib
-    src = os.path.join(ROOT, "transformer_block_lamb_amd", "csrc", "gemm.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("gemm_source_sha256") != digest:
+    if rec.get("gemm_sources_sha256") != gemm_source_digest():
         return None
     return rec.get("stages", {}).get(kernel_stage)
 
