@@ -653,10 +653,14 @@ __device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int l
 // but A_{t+2}) and the workgroup meets at the tile's only barrier; the
 // fourth phase reads tile t+1's first fragments and issues B_{t+2} into
 // A_t's slot.  The slot pattern repeats every five tiles, so the loop is
-// unrolled by five and every LDS address is static; tiles past ke skip
-// their MFMAs but keep their barriers and loads (of tile ke-1) so every
-// wave's load count stays in step with the waits.  RAGGED: K is not a
-// multiple of BK, so the last K tile masks its loads lane by lane.
+// unrolled by five and every LDS address is static.  The last two tiles of
+// a segment still issue the loads of tiles ke and ke + 1 (reloads of tile
+// ke - 1, in L2), so that every multiplied tile's wait counts the same
+// loads; the calls past ke multiply nothing and load nothing, only meet at
+// their barriers (their waits then have fewer loads to count, so they pass
+// once those reloads land), and the loop's end drains what is in flight.
+// RAGGED: K is not a multiple of BK, so the last K tile masks its loads
+// lane by lane.
 template <int ALAY, int BLAY, bool RAGGED, class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
   // one array per slot, so the compiler sees that loads into one slot do
@@ -732,8 +736,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Tiles past ke are never multiplied, but their loads keep every wave's
-    // load count in step with the waits: they reload tile ke-1 (in L2).
+    // Loads for tiles past ke (issued by the segment's last two tiles) reload
+    // tile ke-1 (in L2): they keep those tiles' load counts in step with
+    // their waits.
     auto issue_a = [&](char* st, int t) {
       const int u = t < ke ? t : ke - 1;
       const bool second = u >= nk1;
@@ -763,8 +768,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
         frb.read(fb[1], cb, 3);
         mma_step(acc, fa[0], fb[0]);
         interleave<kReads, 0, 1>();
-      } else {
-        issue_a(sa, t + 2);
       }
       // A_{t+1} and B_{t+1} have landed (A_{t+2}, issued last, may still be
       // in flight) and every wave is done reading tile t
@@ -775,8 +778,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
         issue_b(ca, t + 2);
         mma_step(acc, fa[1], fb[1]);
         interleave<kReads, kDmaPerOp, 1>();
-      } else {
-        issue_b(ca, t + 2);
       }
     };
 
