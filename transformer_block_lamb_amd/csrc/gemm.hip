@@ -653,14 +653,12 @@ __device__ __forceinline__ int partial_off(int wave, int i, int j, int r4, int l
 // but A_{t+2}) and the workgroup meets at the tile's only barrier; the
 // fourth phase reads tile t+1's first fragments and issues B_{t+2} into
 // A_t's slot.  The slot pattern repeats every five tiles, so the loop is
-// unrolled by five and every LDS address is static.  The last two tiles of
-// a segment still issue the loads of tiles ke and ke + 1 (reloads of tile
-// ke - 1, in L2), so that every multiplied tile's wait counts the same
-// loads; the calls past ke multiply nothing and load nothing, only meet at
-// their barriers (their waits then have fewer loads to count, so they pass
-// once those reloads land), and the loop's end drains what is in flight.
-// RAGGED: K is not a multiple of BK, so the last K tile masks its loads
-// lane by lane.
+// unrolled by five and every LDS address is static.  Whole groups of five
+// run while every load they issue is a real tile (t + 2 < ke); the last
+// one to six tiles then go through a copy of the tile step that loads only
+// tiles before ke and waits for exactly the loads in flight (all of them
+// when none is issued ahead).  RAGGED: K is not a multiple of BK, so the
+// last K tile masks its loads lane by lane.
 template <int ALAY, int BLAY, bool RAGGED, class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
   // one array per slot, so the compiler sees that loads into one slot do
@@ -736,9 +734,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Loads for tiles past ke (issued by the segment's last two tiles) reload
-    // tile ke-1 (in L2): they keep those tiles' load counts in step with
-    // their waits.
+    // (only the prologue may load past ke: tile kb + 1 of a one-tile
+    // segment, which reloads tile ke - 1 and is drained by its wait)
     auto issue_a = [&](char* st, int t) {
       const int u = t < ke ? t : ke - 1;
       const bool second = u >= nk1;
@@ -788,13 +785,51 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     wait_barrier<2 * kDmaPerOp>();
     fra.read(fa[0], s0, 0);
     frb.read(fb[0], s1, 0);
-    for (int t = kb; t < ke; t += kSlots) {
+    // The last tiles of the segment (at most six, starting at the first slot
+    // of the pattern): only tiles before ke are loaded, and each wait counts
+    // exactly the loads in flight.
+    auto tile_end = [&](char* ca, char* cb, char* na, char* nb, char* sa, int t) {
+      if (t >= ke) return;  // uniform over the workgroup
+      const bool ahead = t + 2 < ke;
+      if (ahead) issue_a(sa, t + 2);
+      fra.read(fa[1], ca, 1);
+      frb.read(fb[1], cb, 1);
+      mma_step(acc, fa[0], fb[0]);
+      interleave<kReads, kDmaPerOp, 2>();
+      fra.read(fa[0], ca, 2);
+      frb.read(fb[0], cb, 2);
+      mma_step(acc, fa[1], fb[1]);
+      interleave<kReads, 0, 1>();
+      fra.read(fa[1], ca, 3);
+      frb.read(fb[1], cb, 3);
+      mma_step(acc, fa[0], fb[0]);
+      interleave<kReads, 0, 1>();
+      if (ahead)
+        wait_barrier<kDmaPerOp>();
+      else
+        wait_barrier<0>();
+      if (t + 1 < ke) {
+        fra.read(fa[0], na, 0);
+        frb.read(fb[0], nb, 0);
+      }
+      if (ahead) issue_b(ca, t + 2);
+      mma_step(acc, fa[1], fb[1]);
+      interleave<kReads, kDmaPerOp, 1>();
+    };
+    int t = kb;
+    for (; t + kSlots + 1 < ke; t += kSlots) {  // every load of the group is a real tile
       tile(s0, s1, s2, s3, s4, t);
       tile(s2, s3, s4, s0, s1, t + 1);
       tile(s4, s0, s1, s2, s3, t + 2);
       tile(s1, s2, s3, s4, s0, t + 3);
       tile(s3, s4, s0, s1, s2, t + 4);
     }
+    tile_end(s0, s1, s2, s3, s4, t);
+    tile_end(s2, s3, s4, s0, s1, t + 1);
+    tile_end(s4, s0, s1, s2, s3, t + 2);
+    tile_end(s1, s2, s3, s4, s0, t + 3);
+    tile_end(s3, s4, s0, s1, s2, t + 4);
+    tile_end(s0, s1, s2, s3, s4, t + 5);
     __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing LDS
     __syncthreads();
 
