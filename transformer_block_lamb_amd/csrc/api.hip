@@ -265,7 +265,7 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
         GemmDesc g{(int)d.K2, (int)d.h, (int)d.T, kMNContig, kMNContig, cat, d.K2, dy, d.h};
         g.ws = ws;
         g.ws_bytes = ws_bytes;
-        e = launch_gemm_store(dt, g, dw_out, d.h, false, stream);
+        e = launch_gemm_store(dt, g, dw_out, d.h, false, stream, true);
         break;
       }
       case PTB_BWD_ATTENTION:  // -> dz[:, :3A]
@@ -275,7 +275,7 @@ int ptb_backward_stage(const ptb_dims* dims, int32_t stage, const void* x, const
         GemmDesc g{(int)d.N1, (int)d.h, (int)d.T, kMNContig, kMNContig, dz, d.N1, xn, d.h};
         g.ws = ws;
         g.ws_bytes = ws_bytes;
-        e = launch_gemm_store(dt, g, dw_in, d.h, false, stream);
+        e = launch_gemm_store(dt, g, dw_in, d.h, false, stream, true);
         break;
       }
       case PTB_BWD_GEMM_DXN: {  // dxn = dz w_in
@@ -487,7 +487,7 @@ int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_ga
   // MLP sub-layer: dw_fc2 = GeLU(f)^T dy; df = (dy w_fc2^T) GeLU'(f) into dz[:, 3A:]
   hipError_t e = launch_gemm_store(
       dt, gemm((int)d.F, (int)d.h, (int)d.T, kMNContig, kMNContig, off(cat, d.A, d.e), d.K2, dy, d.h),
-      dw_out_c + d.A * d.h * d.e, d.h, false, stream);
+      dw_out_c + d.A * d.h * d.e, d.h, false, stream, true);
   if (e == hipSuccess)
     e = launch_gemm_dcat(dt, gemm((int)d.T, (int)d.F, (int)d.h, kKContig, kKContig, dy, d.h,
                                   off(w_out, d.A * d.h, d.e), d.h),
@@ -495,7 +495,7 @@ int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_ga
   if (e == hipSuccess)  // dw_fc1 = df^T xn2
     e = launch_gemm_store(dt, gemm((int)d.F, (int)d.h, (int)d.T, kMNContig, kMNContig,
                                    off(dz, 3 * d.A, d.e), d.N1, xn2, d.h),
-                          dw_in_c + 3 * d.A * d.h * d.e, d.h, false, stream);
+                          dw_in_c + 3 * d.A * d.h * d.e, d.h, false, stream, true);
   if (e == hipSuccess)  // dxn2 = df w_fc1
     e = launch_gemm_store(dt, gemm((int)d.T, (int)d.h, (int)d.F, kKContig, kMNContig,
                                    off(dz, 3 * d.A, d.e), d.N1, off(w_in, 3 * d.A * d.h, d.e), d.h),
@@ -509,7 +509,7 @@ int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_ga
   if (e == hipSuccess)
     e = launch_gemm_store(dt, gemm((int)d.A, (int)d.h, (int)d.T, kMNContig, kMNContig, cat, d.K2,
                                    dh, d.h),
-                          dw_out, d.h, false, stream);
+                          dw_out, d.h, false, stream, true);
   if (e == hipSuccess)
     e = launch_gemm_dcat(dt, gemm((int)d.T, (int)d.A, (int)d.h, kKContig, kKContig, dh, d.h, w_out,
                                   d.h),
@@ -520,7 +520,7 @@ int ptb_serial_backward(const ptb_dims* dims, const void* x, const float* ln1_ga
   if (e == hipSuccess)  // dw_qkv = dqkv^T xn1
     e = launch_gemm_store(dt, gemm((int)(3 * d.A), (int)d.h, (int)d.T, kMNContig, kMNContig, dz,
                                    d.N1, xn1, d.h),
-                          dw_in, d.h, false, stream);
+                          dw_in, d.h, false, stream, true);
   if (e == hipSuccess)  // dxn1 = dqkv w_qkv
     e = launch_gemm_store(dt, gemm((int)d.T, (int)d.h, (int)(3 * d.A), kKContig, kMNContig, dz,
                                    d.N1, w_in, d.h),

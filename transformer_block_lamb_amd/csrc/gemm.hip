@@ -113,11 +113,23 @@ template <typename T>
 struct EpiStore {
   T* c;
   int64_t ldc;
+  int nt = 0;  // bf16: whole chunks bypass the caches (non-temporal stores)
   __device__ __forceinline__ void operator()(int row, int col, float v) const {
     Elt<T>::st(c + (int64_t)row * ldc + col, v);
   }
   __device__ __forceinline__ void store8(int row, int col, const float (&v)[8], int ncols) const {
-    put8(c + (int64_t)row * ldc + col, v, ncols - col);
+    T* p = c + (int64_t)row * ldc + col;
+    if constexpr (sizeof(T) == 2) {
+      if (nt && ncols - col >= 8) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 u;
+        u.x = pack_bf2(v[0], v[1]); u.y = pack_bf2(v[2], v[3]);
+        u.z = pack_bf2(v[4], v[5]); u.w = pack_bf2(v[6], v[7]);
+        __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
+        return;
+      }
+    }
+    put8(p, v, ncols - col);
   }
   struct Pre {};
   __device__ __forceinline__ void pre8(int, int, Pre&, int) const {}
@@ -1139,10 +1151,11 @@ hipError_t run_layouts(const GemmDesc& d, const Epi& epi, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_store(int dtype, const GemmDesc& d, void* c, int64_t ldc, bool c_f32,
-                             hipStream_t s) {
+                             hipStream_t s, bool streaming) {
   if (dtype == 1) {
     if (c_f32) return run_layouts<EpiStore<float>, true>(d, EpiStore<float>{(float*)c, ldc}, s);
-    return run_layouts<EpiStore<bf16_t>, true>(d, EpiStore<bf16_t>{(bf16_t*)c, ldc}, s);
+    return run_layouts<EpiStore<bf16_t>, true>(
+        d, EpiStore<bf16_t>{(bf16_t*)c, ldc, streaming ? 1 : 0}, s);
   }
   return run_layouts<EpiStore<float>, false>(d, EpiStore<float>{(float*)c, ldc}, s);
 }

@@ -49,9 +49,11 @@ hipError_t launch_ln_bwd_reduce(const float* gpart, const float* bpart, int nblk
                                 float* dgamma, float* dbeta, hipStream_t s);
 
 // ---- gemm.hip
-// Plain product stored in the operand dtype (or fp32 when c_f32).
+// Plain product stored in the operand dtype (or fp32 when c_f32).  streaming:
+// bf16 output written with non-temporal stores, for products that nothing
+// reads before they would have left the caches anyway (the weight gradients).
 hipError_t launch_gemm_store(int dtype, const GemmDesc& g, void* c, int64_t ldc, bool c_f32,
-                             hipStream_t s);
+                             hipStream_t s, bool streaming = false);
 // Input projection of the block: columns < qkv_cols (3A for the fused
 // projection, 0 for FC1 alone) go to qkv [T, qkv_cols] (and, for the q and
 // k columns, their bf16 rounding residual to qk_lo [T, 2A] when qk_lo is not
