@@ -707,14 +707,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   int64_t it = g.sk ? sk_lo(g, gl) : 0;
   const int64_t it_end = g.sk ? sk_lo(g, gl + 1) : 0;
   bool first_sk = true;
-  // With both whole tiles and a split range, every other pair of workers
-  // (pairs of consecutive ranges, which share a tile when tiles split in
-  // two) runs its split range first: the whole-tile epilogues and the split
-  // tiles' fix-ups then come in two waves of half the chip each.
-  const bool split_first = g.sk && ((gl >> 1) & 1);
   for (;;) {
     int tm, tn, kb, ke, slot = -1, lt = 0;
-    if (dp_left > 0 && !(split_first && it < it_end)) {
+    if (dp_left > 0) {
       if (g.sk) {
         g.sc.tile(dp_next, tm, tn);
         dp_next += per;
