@@ -46,7 +46,14 @@ constexpr int kGemmThreads = 64 * kWaves;
 constexpr int kGroupM = 8;
 
 // --------------------------------------------------------------- epilogues
-// Each epilogue takes one accumulator value (operator(), used by the fp32
+// An LDS (address space 3) view of 16 bytes, so reads of prefetched epilogue
+// operands stay LDS reads (not generic loads merged with the memory path).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_uint4_t;
+__device__ __forceinline__ uint4 lds_read16(const lds_uint4_t* src) {
+  const u32x4_t t = *src;
+  return make_uint4(t.x, t.y, t.z, t.w);
+}// Each epilogue takes one accumulator value (operator(), used by the fp32
 // kernel) or 8 consecutive columns of one row (used by the MFMA kernel after
 // staging through LDS; col % 8 == 0, columns >= ncols dropped) in two steps:
 // pre8 loads whatever else the columns need (the residual, the FC1
@@ -132,6 +139,7 @@ struct EpiStore {
     put8(p, v, ncols - col);
   }
   struct Pre {};
+  static constexpr bool kOperand = false;
   __device__ __forceinline__ void pre8(int, int, Pre&, int) const {}
   __device__ __forceinline__ void store8p(int row, int col, const float (&v)[8], const Pre&,
                                           int ncols) const {
@@ -178,6 +186,7 @@ struct EpiInFwd {
     }
   }
   struct Pre {};
+  static constexpr bool kOperand = false;
   __device__ __forceinline__ void pre8(int, int, Pre&, int) const {}
   __device__ __forceinline__ void store8p(int row, int col, const float (&v)[8], const Pre&,
                                           int ncols) const {
@@ -199,6 +208,22 @@ struct EpiOutFwd {
   using Pre = Raw8<T>;
   __device__ __forceinline__ void pre8(int row, int col, Pre& p, int ncols) const {
     if (add) p.load(x + (int64_t)row * ld + col, ncols - col);
+  }
+  // The residual as an LDS-prefetched operand (bf16): whole 8-column chunks
+  // only; a chunk cut by the matrix edge is read from memory at use.
+  static constexpr bool kOperand = sizeof(T) == 2;
+  __device__ __forceinline__ bool has_op(int) const { return add != 0; }
+  __device__ __forceinline__ const void* op_base() const { return x; }
+  __device__ __forceinline__ uint32_t op_bytes(int M) const {
+    return (uint32_t)((int64_t)M * ld * sizeof(T));
+  }
+  __device__ __forceinline__ uint32_t op_off(int row, int col, int M, int ncols) const {
+    return row < M && col + 8 <= ncols ? (uint32_t)(((int64_t)row * ld + col) * sizeof(T))
+                                       : kOutOfRange;
+  }
+  __device__ __forceinline__ void pre8_lds(int, int col, Pre& p, int ncols,
+                                           const lds_uint4_t* src) const {
+    if (ncols - col >= 8) p.u = lds_read16(src);
   }
   __device__ __forceinline__ void store8p(int row, int col, const float (&v)[8], const Pre& p,
                                           int ncols) const {
@@ -239,6 +264,10 @@ struct EpiDcat {
   __device__ __forceinline__ void pre8(int row, int col, Pre& p, int ncols) const {
     if (col >= attn) p.load(f + (int64_t)row * ffn + (col - attn), ncols - col);
   }
+  // f stays a memory load: prefetching it into LDS one strip ahead, as the
+  // residual is, measured 1-2 us slower (its reads are bandwidth-bound when
+  // every CU runs this epilogue at once).
+  static constexpr bool kOperand = false;
   __device__ __forceinline__ void store8p(int row, int col, const float (&v)[8], const Pre& p,
                                           int ncols) const {
     const int valid = ncols - col;
@@ -613,12 +642,24 @@ __device__ __forceinline__ void wait_barrier() {
 constexpr int kStageRow = 36, kStageBlk = 1216;
 template <class Epi>
 __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* stage, int row0,
-                                               int col0, int lane, int M, int N, const Epi& epi) {
+                                               int col0, int lane, int M, int N, const Epi& epi,
+                                               bool use_op = false, const char* opbuf = nullptr,
+                                               bool op_last = false) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float* blk = stage + j * kStageBlk + j * 4;
 #pragma unroll
     for (int r = 0; r < 16; ++r) blk[mfma32_row(r, lane) * kStageRow + (lane & 31)] = a[j][r];
+  }
+  if constexpr (Epi::kOperand) {
+    // prefetched operand: this strip's chunks (the wave's own LDS-bound
+    // loads) have landed once at most the next strip's four loads remain
+    if (use_op) {
+      if (op_last)
+        __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0)
+      else
+        __builtin_amdgcn_s_waitcnt(4 | (7 << 4));  // vmcnt(4) lgkmcnt(0)
+    }
   }
   __syncthreads();
   constexpr int kChunks = 32 * 8 / 64;  // 8-column chunks of the 32x64 strip per lane
@@ -634,7 +675,16 @@ __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* st
     v[q][0] = lo.x; v[q][1] = lo.y; v[q][2] = lo.z; v[q][3] = lo.w;
     v[q][4] = hi.x; v[q][5] = hi.y; v[q][6] = hi.z; v[q][7] = hi.w;
     const int row = row0 + rr, col = col0 + j * 32 + c8;
-    if (row < M && col < N) epi.pre8(row, col, pre[q], N);
+    if (row < M && col < N) {
+      if constexpr (Epi::kOperand) {
+        if (use_op)
+          epi.pre8_lds(row, col, pre[q], N, (const lds_uint4_t*)(opbuf + q * 1024 + lane * 16));
+        else
+          epi.pre8(row, col, pre[q], N);
+      } else {
+        epi.pre8(row, col, pre[q], N);
+      }
+    }
   }
 #pragma unroll
   for (int q = 0; q < kChunks; ++q) {
@@ -645,6 +695,30 @@ __device__ __forceinline__ void epilogue_strip(const f32x16_t (&a)[2], float* st
   }
   __syncthreads();
 }
+
+// LDS-bound loads of one strip's epilogue operand chunks (the 32 x 64 strip
+// at row0, col0, in the chunk order epilogue_strip reads) into this wave's
+// 4 KB area `dst`: four wave instructions, lane L's chunk q at
+// dst + 1024 q + 16 L.  Chunks without an operand load zeros.
+template <class Epi>
+struct OperandLoads {
+  __amdgpu_buffer_rsrc_t rs;
+  __device__ __forceinline__ void init(const Epi& epi, int M) {
+    rs = make_rsrc(epi.op_base(), epi.op_bytes(M));
+  }
+  __device__ __forceinline__ void issue(const Epi& epi, char* dst, int row0, int col0, int lane,
+                                        int M, int N) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = lane + 64 * q;
+      const int rr = c >> 3, jc = c & 7, j = jc >> 2, c8 = (jc & 3) * 8;
+      // (the offset goes through a local: passing the call itself as the
+      // builtin's argument made the compiler drop the host launch stubs)
+      const uint32_t vo = epi.op_off(row0 + rr, col0 + j * 32 + c8, M, N);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + q * 1024), 16, vo, 0, 0, 0);
+    }
+  }
+};
 
 // Offset (floats) of this lane's accumulators acc[i][j][4 r4 .. 4 r4 + 3] in
 // a partial tile: one 1 KB run per (wave, i, j, r4), so each store or load
@@ -846,9 +920,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     __syncthreads();
 
     if (slot < 0) {
+      // An epilogue operand (the residual, bf16) comes into the idle slots
+      // s3 / s4 with LDS-bound loads one strip ahead: each lane loads exactly
+      // the four 16-byte chunks it combines later, so it reads back its own
+      // data (4 KB per wave and strip, four loads per lane), and a strip
+      // waits with vmcnt(4) for its own chunks.
+      bool pf = false;
+      if constexpr (Epi::kOperand) pf = epi.has_op(n0);
+      char* const ob0 = s3 + wave * 4096;
+      char* const ob1 = s4 + wave * 4096;
+      const int orow = m0 + wm * 128, ocol = n0 + wn * 64;
+      if constexpr (Epi::kOperand) {
+        if (pf) {
+          OperandLoads<Epi> ol;
+          ol.init(epi, g.M);
+          ol.issue(epi, ob0, orow, ocol, lane, g.M, g.N);
+          ol.issue(epi, ob1, orow + 32, ocol, lane, g.M, g.N);
+        }
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        epilogue_strip(acc[i], stage, m0 + wm * 128 + i * 32, n0 + wn * 64, lane, g.M, g.N, epi);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (Epi::kOperand) {
+          if (pf && i >= 1 && i <= 2) {
+            OperandLoads<Epi> ol;
+            ol.init(epi, g.M);
+            ol.issue(epi, (i & 1) ? ob0 : ob1, orow + (i + 1) * 32, ocol, lane, g.M, g.N);
+          }
+        }
+        epilogue_strip(acc[i], stage, m0 + wm * 128 + i * 32, n0 + wn * 64, lane, g.M, g.N, epi,
+                       pf, (i & 1) ? ob1 : ob0, i == 3);
+      }
     } else {
       // Partials move with device-scope (sc1) buffer stores and loads, which
       // other XCDs see without a writeback or invalidation of the whole L2.
